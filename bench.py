@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-layer MoE training hot path on one MI355X.
+
+One step = moe_dispatch_build + moe_ffn_forward + moe_ffn_backward on one
+batch of synthetic inputs already resident in HBM.  Prints one JSON line:
+routed tokens/s (L per step time), per-kernel times from HIP events recorded
+by the library on the launch stream, the roofline of the dominant kernel,
+the dispatch builder's HBM roofline, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from token_dispatch_expert_amd import binding as B  # noqa: E402
+from token_dispatch_expert_amd import workloads as W  # noqa: E402
+from token_dispatch_expert_amd.layer import MoELayerBuffers  # noqa: E402
+
+PEAK_TFLOPS = {W.BF16: 2500.0, W.F32: 157.3}   # dense MFMA peaks of MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_flops(cfg):
+    """Algorithmic flops of ONE launch of each GEMM kernel."""
+    L, d, h, K, R = cfg.L, cfg.d, cfg.h, cfg.K, cfg.R
+    nproj = 2 if cfg.act == W.SWIGLU else 1
+    return {
+        "ffn_f1_gather_glu": 2 * R * d * h * nproj,
+        "ffn_f2_down_combine": 2 * L * h * d,          # one slot pass: L routes
+        "ffn_b1_dgrad_glu": 2 * R * d * h,
+        "ffn_b0_dw2": 2 * R * h * d,
+        "ffn_b2_dw13": 2 * R * d * h * nproj,
+        "ffn_b3_dx": 2 * L * d * h * nproj,            # one slot pass
+    }
+
+
+def dispatch_bytes(cfg):
+    """Algorithmic HBM bytes of one dispatch build: logits read (4LE), the
+    uint8 token-expert map written once and read once (2LE), the four L*K
+    int32/float32 outputs token_expert_indices, gates, expert_token_indices,
+    token_index_map (16LK), and the offsets."""
+    return 4 * cfg.L * cfg.E + 2 * cfg.L * cfg.E + 16 * cfg.L * cfg.K + 4 * (cfg.E + 1)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "token_dispatch_expert_amd", "csrc"))):
+        with open(os.path.join(ROOT, "token_dispatch_expert_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s=15.0):
+    """The oracle, untuned, on a bounded prefix sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 0) for i in info] or [0])
+    except Exception:  # noqa: BLE001
+        threads = 0
+    if threads <= 0:
+        threads = int(os.environ.get("OPENBLAS_NUM_THREADS")
+                      or os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+
+    W1 = inp["W1"].float().cpu().numpy()
+    W3 = inp["W3"].float().cpu().numpy() if inp["W3"] is not None else None
+    W2 = inp["W2"].float().cpu().numpy()
+
+    def run(n):
+        z = inp["logits"][:n].cpu().numpy()
+        x = inp["x"][:n].float().cpu().numpy()
+        dy = inp["dy"][:n].float().cpu().numpy()
+        t0 = time.perf_counter()
+        tei, gates = oracle.route(z, cfg.K)
+        eti, off, tim = oracle.build_indices(tei, cfg.E)
+        oracle.ffn_forward(x, W1, W3, W2, eti, off, tim, gates, cfg.act)
+        oracle.ffn_backward(dy, x, W1, W3, W2, eti, off, tim, gates, cfg.act)
+        return time.perf_counter() - t0
+
+    n = min(256, cfg.L)
+    t = run(n)
+    while t < budget_s / 4 and n < cfg.L:
+        n = min(cfg.L, max(n * 2, int(n * budget_s / max(t, 1e-3) / 2)))
+        t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} tokens of the workload (same d, h, E, K, weights), "
+                      f"dispatch + forward + backward in float64 numpy, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
+              "and has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = W.CONFIGS[args.config]
+    seed = args.config if args.seed is None else args.seed
+    dev = torch.device("cuda:0")
+    log(f"[bench] {cfg.name}: generating inputs on {torch.cuda.get_device_name(0)}")
+    inp = W.make_inputs(cfg, seed, dev)
+    buf = MoELayerBuffers(cfg, dev)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        buf.step(inp)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    B.profile_reset()
+    B.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        buf.step(inp)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.profile_enable(False)
+    stats = B.profile_read()
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+
+    ms_step = elapsed * 1e3 / args.steps
+    kflops = kernel_flops(cfg)
+    per_kernel = {k: {"launches_per_step": n / args.steps, "ms_per_step": ms / args.steps,
+                      "avg_launch_ms": ms / max(n, 1)} for k, (n, ms) in stats.items()}
+    gemm = {k: v for k, v in per_kernel.items() if k in kflops}
+    dom = max(gemm, key=lambda k: gemm[k]["ms_per_step"])
+    avg_s = gemm[dom]["avg_launch_ms"] / 1e3
+    achieved = kflops[dom] / avg_s / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    for k, v in per_kernel.items():
+        if k in kflops:
+            v["tflops"] = kflops[k] / (v["avg_launch_ms"] / 1e3) / 1e12
+    gemm_ms = sum(v["ms_per_step"] for v in gemm.values())
+    total_flops = sum(kflops[k] * gemm[k]["launches_per_step"] for k in gemm)
+
+    disp_keys = ("dispatch_route_map", "dispatch_expert_scan", "dispatch_scatter")
+    disp_ms = sum(per_kernel[k]["ms_per_step"] for k in disp_keys if k in per_kernel)
+    disp_gbs = dispatch_bytes(cfg) / (disp_ms / 1e3) / 1e9 if disp_ms > 0 else None
+
+    traffic = measured_traffic(dom, cfg.name)
+    out = {
+        "metric": "routed tokens/sec (MoE layer fwd+bwd, 1 GPU)",
+        "value": cfg.L / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == W.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "L": cfg.L, "d": cfg.d, "h": cfg.h, "E": cfg.E,
+                   "K": cfg.K, "act": "swiglu" if cfg.act == W.SWIGLU else "silu",
+                   "seed": seed, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                     "flops_per_launch": kflops[dom],
+                     "avg_launch_ms": gemm[dom]["avg_launch_ms"]},
+        "roofline_dispatch": {"bound": "hbm", "achieved": disp_gbs, "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s",
+                              "frac": (disp_gbs / PEAK_HBM_GBS) if disp_gbs else None,
+                              "bytes_per_build": dispatch_bytes(cfg), "ms_per_build": disp_ms},
+        "assignments_per_s": cfg.R / (ms_step / 1e3),
+        "gemm_tflops_all": total_flops / (gemm_ms / 1e3) / 1e12,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/moe_dispatch.h declares, and rejects bad arguments before any
+HIP call (so no compute is launched here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from token_dispatch_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from token_dispatch_expert_amd import build_lib
+        build_lib.build(verbose=False)
+    return B.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("moe_dispatch_build", "moe_ffn_forward", "moe_ffn_backward", "moe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    assert set(B.EXPORTED) == set(declared_functions())
+
+
+FAKE = 4096  # 16-byte aligned placeholder address, never dereferenced: every call
+# below either fails validation or stops at the workspace-size check (nbytes=0),
+# so nothing is launched
+
+
+def call_build(lib, shape, ptrs=None, ws=FAKE, nbytes=0):
+    p = ptrs or [FAKE] * 6
+    n = ctypes.c_size_t(nbytes)
+    rc = lib.moe_dispatch_build(ctypes.byref(shape) if shape is not None else None, *p,
+                                ws, ctypes.byref(n), None)
+    return rc, n.value
+
+
+def call_fwd(lib, shape, ptrs=None, ws=FAKE, nbytes=0):
+    p = ptrs or [FAKE] * 12
+    n = ctypes.c_size_t(nbytes)
+    rc = lib.moe_ffn_forward(ctypes.byref(shape), *p, ws, ctypes.byref(n), None)
+    return rc, n.value
+
+
+def call_bwd(lib, shape, ptrs=None, ws=FAKE, nbytes=0):
+    p = ptrs or [FAKE] * 16
+    n = ctypes.c_size_t(nbytes)
+    rc = lib.moe_ffn_backward(ctypes.byref(shape), *p, ws, ctypes.byref(n), None)
+    return rc, n.value
+
+
+GOOD = dict(L=1024, d=64, h=128, E=8, K=2, dtype=B.MOE_BF16, act=B.MOE_SWIGLU)
+
+
+def shp(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return B.make_shape(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), B.MOE_ERR_INVALID_ARG),
+    (dict(L=-5), B.MOE_ERR_INVALID_ARG),
+    (dict(E=0), B.MOE_ERR_INVALID_ARG),
+    (dict(K=0), B.MOE_ERR_INVALID_ARG),
+    (dict(K=9), B.MOE_ERR_INVALID_ARG),
+    (dict(E=257, K=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=256, K=256), B.MOE_ERR_UNSUPPORTED),
+    (dict(L=1 << 30, K=2), B.MOE_ERR_UNSUPPORTED),
+])
+def test_routing_shape_errors(lib, kw, code):
+    rc, _ = call_build(lib, shp(**kw))
+    assert rc == code
+    assert lib.moe_last_error().decode()
+    rc, _ = call_fwd(lib, shp(**kw))
+    assert rc == code
+    rc, _ = call_bwd(lib, shp(**kw))
+    assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), B.MOE_ERR_INVALID_ARG),
+    (dict(act=3), B.MOE_ERR_INVALID_ARG),
+    (dict(d=0), B.MOE_ERR_INVALID_ARG),
+    (dict(h=-8), B.MOE_ERR_INVALID_ARG),
+    (dict(d=60), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=100), B.MOE_ERR_UNSUPPORTED),
+])
+def test_ffn_shape_errors(lib, kw, code):
+    assert call_fwd(lib, shp(**kw))[0] == code
+    assert call_bwd(lib, shp(**kw))[0] == code
+
+
+def test_null_shape(lib):
+    n = ctypes.c_size_t(0)
+    rc = lib.moe_dispatch_build(None, *([FAKE] * 6), FAKE, ctypes.byref(n), None)
+    assert rc == B.MOE_ERR_INVALID_ARG
+    assert "shape" in lib.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_build_null_or_misaligned_pointer(lib, i):
+    p = [FAKE] * 6
+    p[i] = None
+    assert call_build(lib, shp(), p)[0] == B.MOE_ERR_INVALID_ARG
+    p[i] = FAKE + 2
+    assert call_build(lib, shp(), p)[0] == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_forward_null_or_misaligned_pointer(lib, i):
+    p = [FAKE] * 12
+    p[i] = None
+    assert call_fwd(lib, shp(), p)[0] == B.MOE_ERR_INVALID_ARG
+    # W3 (index 2) and B (index 11) may be NULL for SiLU
+    if i in (2, 11):
+        assert call_fwd(lib, shp(act=B.MOE_SILU), p, ws=None)[0] == B.MOE_OK
+    p[i] = FAKE + 4
+    rc = call_fwd(lib, shp(), p)[0]
+    if i in (4, 5, 6, 7, 8):     # int32 / float32 arrays need only 4-byte alignment
+        assert rc == B.MOE_ERR_WORKSPACE       # reaches the workspace check
+    else:
+        assert rc == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_backward_null_pointer(lib, i):
+    p = [FAKE] * 16
+    p[i] = None
+    assert call_bwd(lib, shp(), p)[0] == B.MOE_ERR_INVALID_ARG
+    if i in (3, 11, 14):          # W3, B, dW3 unused for SiLU
+        assert call_bwd(lib, shp(act=B.MOE_SILU), p, ws=None)[0] == B.MOE_OK
+
+
+def test_workspace_query_and_too_small(lib):
+    for call, n in ((call_build, 6), (call_fwd, 12), (call_bwd, 16)):
+        rc, need = call(lib, shp(), ws=None, nbytes=0)
+        assert rc == B.MOE_OK and need > 0
+        rc, _ = call(lib, shp(), ws=FAKE, nbytes=need - 1)
+        assert rc == B.MOE_ERR_WORKSPACE
+        assert "workspace" in lib.moe_last_error().decode()
+        rc, _ = call(lib, shp(), ws=FAKE + 16, nbytes=need)
+        assert rc == B.MOE_ERR_INVALID_ARG          # ws must be 256-byte aligned
+    n = ctypes.c_size_t(0)
+    assert lib.moe_dispatch_build(ctypes.byref(shp()), *([FAKE] * 6), None, None, None) \
+        == B.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_L(lib):
+    a = B.workspace_bytes("moe_ffn_forward", shp(L=1000))
+    b = B.workspace_bytes("moe_ffn_forward", shp(L=100000))
+    assert b > a
+    # forward keeps a [L*K, h] activation buffer and a float32 [L, d] accumulator
+    L, K, h, d = 100000, 2, 128, 64
+    assert b >= L * K * h * 2 + L * d * 4
+    # float32 output needs no separate accumulator
+    c = B.workspace_bytes("moe_ffn_forward", shp(L=100000, dtype=B.MOE_F32))
+    assert c >= L * K * h * 4
+
+
+def test_profile_calls_without_gpu(lib):
+    assert lib.moe_profile_enable(0) == B.MOE_OK
+    assert lib.moe_profile_reset() == B.MOE_OK
+    n = ctypes.c_int(-1)
+    assert lib.moe_profile_read(None, 0, ctypes.byref(n)) == B.MOE_OK
+    assert n.value >= 0

@@ -1,0 +1,269 @@
+// Atomic-free construction of the routing index structures on gfx950.
+//
+// The three steps follow the MoEBlaze wiki note, "Core method" >
+// "atomic-free three-step dispatch construction":
+//   1. a dense token-expert map, each (expert, token) entry written once;
+//   2. per-expert length counts by reduction, then a prefix sum for the
+//      expert offsets;
+//   3. a scan inside each tile of the map gives every selected entry its
+//      final place in the per-expert token list, then a parallel write.
+//
+// MI355X layout.  The map is stored expert-major, [E][Lpad] bytes, holding
+// slot+1 for a selected entry and 0 otherwise (the slot is needed to fill
+// token_index_map).  Step 1 routes one tile of T tokens per workgroup and
+// transposes its part of the map through LDS so that every map row segment
+// leaves as full 16-byte stores; as a by-product it counts each expert's
+// entries in the tile, so step 2 only has to scan E x C tile counts (one
+// workgroup per expert column) instead of re-reading the map.  Step 3 reads
+// each row segment once with 16-byte loads, one wavefront per expert row.
+// No kernel uses atomics; every output element has exactly one writer.
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+#include <limits.h>
+
+namespace moe {
+
+// Step 1: top-K routing, gates, map tile, per-tile expert counts.
+// G lanes cooperate on one token; lane j of the group owns experts
+// 4j .. 4j+3.  The K winners are found by K rounds of a group arg-max (ties
+// to the lower expert id); the softmax and the ascending-expert slot order
+// come from group reductions and a group prefix count.
+template <int G, bool VEC4>
+__global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ logits, int64_t L,
+                                                    int E, int K, int T, int C, int64_t Lpad,
+                                                    int32_t* __restrict__ tei,
+                                                    float* __restrict__ gates,
+                                                    uint8_t* __restrict__ map,
+                                                    int32_t* __restrict__ tilecnt) {
+  __shared__ __attribute__((aligned(16))) uint8_t smap[65536];  // [E][T]
+  const int tile = blockIdx.x;
+  const int64_t t0 = (int64_t)tile * T;
+  const int nvec = (E * T) >> 4;
+  for (int i = threadIdx.x; i < nvec; i += 256) reinterpret_cast<uint4*>(smap)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  const int lg = threadIdx.x & (G - 1);
+  constexpr int NG = 256 / G;
+  for (int tl = threadIdx.x / G; tl < T; tl += NG) {
+    const int64_t t = t0 + tl;
+    if (t >= L) break;
+    const float* row = logits + t * E;
+    float v[4];
+    int ev[4];
+    if (VEC4) {
+      float4 q = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (lg * 4 < E) q = *reinterpret_cast<const float4*>(row + lg * 4);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ev[j] = lg * 4 + j;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ev[j] = lg * 4 + j;
+        v[j] = ev[j] < E ? row[ev[j]] : -INFINITY;
+      }
+    }
+    unsigned sel = 0;
+    float vmax = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float bv = -INFINITY;
+      int be = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool cand = !((sel >> j) & 1u) && ev[j] < E;
+        if (cand && (v[j] > bv || (v[j] == bv && ev[j] < be))) {
+          bv = v[j];
+          be = ev[j];
+        }
+      }
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, G);
+        const int oe = __shfl_xor(be, o, G);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (k == 0) vmax = bv;
+      if ((be >> 2) == lg) sel |= 1u << (be & 3);
+    }
+    float ssum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((sel >> j) & 1u) ssum += expf(v[j] - vmax);
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) ssum += __shfl_xor(ssum, o, G);
+    const int c = __popc(sel);
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) {
+      const int u = __shfl_up(inc, o, G);
+      if (lg >= o) inc += u;
+    }
+    int slot = inc - c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((sel >> j) & 1u) {
+        tei[t * K + slot] = ev[j];
+        gates[t * K + slot] = expf(v[j] - vmax) / ssum;
+        smap[ev[j] * T + tl] = (uint8_t)(slot + 1);
+        ++slot;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nv = T >> 4;
+  for (int e = wave; e < E; e += 4) {
+    int cnt = 0;
+    for (int i = lane; i < nv; i += 64) {
+      const uint4 q = *reinterpret_cast<const uint4*>(smap + e * T + i * 16);
+      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = q;
+      cnt += nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) tilecnt[(int64_t)e * C + tile] = cnt;
+  }
+}
+
+// Exclusive scan of each row of a [rows][C] count table (one workgroup per
+// row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
+// the row sum when total is not null.
+__global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt, int C,
+                                                int64_t row_offset, int32_t* __restrict__ base,
+                                                int32_t* __restrict__ total) {
+  __shared__ int scratch[4];
+  const int r = blockIdx.x;
+  int run = 0;
+  for (int c0 = 0; c0 < C; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const int v = c < C ? cnt[(int64_t)r * C + c] : 0;
+    int tot;
+    const int inc = block256_incl_scan(v, scratch, &tot);
+    if (c < C) base[(int64_t)r * C + c] = (int32_t)(r * row_offset + run + inc - v);
+    run += tot;
+  }
+  if (total != nullptr && threadIdx.x == 0) total[r] = run;
+}
+
+// Step 3: per tile, scan each expert's map row segment and scatter.
+__global__ __launch_bounds__(256) void k3_scatter(const uint8_t* __restrict__ map, int64_t Lpad,
+                                                  int E, int K, int T, int C,
+                                                  const int32_t* __restrict__ tilebase,
+                                                  const int32_t* __restrict__ total,
+                                                  int32_t* __restrict__ eti,
+                                                  int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ tim) {
+  __shared__ int s_off[257];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const int v = tid < E ? total[tid] : 0;
+  int tot;
+  const int inc = block256_incl_scan(v, scratch, &tot);
+  if (tid < E) s_off[tid] = inc - v;
+  if (tid == 0) s_off[E] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) offsets[tid] = s_off[tid];
+    if (tid == 0) offsets[E] = s_off[E];
+  }
+
+  const int tile = blockIdx.x;
+  const int64_t t0 = (int64_t)tile * T;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int e = wave; e < E; e += 4) {
+    int base = s_off[e] + tilebase[(int64_t)e * C + tile];
+    const uint8_t* row = map + (int64_t)e * Lpad + t0;
+    for (int c0 = 0; c0 < T; c0 += 1024) {
+      const int off = c0 + lane * 16;
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (off < T) q = *reinterpret_cast<const uint4*>(row + off);
+      const int cnt = nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
+      const int incl = wave_incl_scan(cnt, lane);
+      int pos = base + incl - cnt;
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const uint32_t val = (w[b >> 2] >> ((b & 3) * 8)) & 0xffu;
+        if (val) {
+          const int64_t t = t0 + off + b;
+          eti[pos] = (int32_t)t;
+          tim[t * K + (val - 1)] = pos;
+          ++pos;
+        }
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  }
+}
+
+void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, int32_t* base,
+                     int32_t* total, hipStream_t s) {
+  hipLaunchKernelGGL(seg_scan, dim3(rows), dim3(256), 0, s, cnt, C, row_offset, base, total);
+}
+
+DispatchPlan plan_dispatch(int64_t L, int E, int K) {
+  (void)K;
+  DispatchPlan p;
+  int T = (65536 / E) / 256 * 256;
+  if (T > 1024) T = 1024;
+  if (T < 256) T = 256;
+  p.T = T;
+  p.C = (int)((L + T - 1) / T);
+  p.Lpad = (int64_t)p.C * T;
+  size_t o = 0;
+  p.off_map = o;   o = align_up(o + (size_t)E * p.Lpad, 256);
+  p.off_cnt = o;   o = align_up(o + (size_t)E * p.C * 4, 256);
+  p.off_base = o;  o = align_up(o + (size_t)E * p.C * 4, 256);
+  p.off_total = o; o = align_up(o + 256 * 4, 256);
+  p.bytes = o;
+  return p;
+}
+
+template <int G>
+static void launch_k1(const DispatchPlan& pl, int64_t L, int E, int K, const float* logits,
+                      int32_t* tei, float* gates, uint8_t* map, int32_t* cnt, hipStream_t s) {
+  const bool vec4 = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  if (vec4)
+    hipLaunchKernelGGL((k1_route_map<G, true>), dim3(pl.C), dim3(256), 0, s, logits, L, E, K, pl.T,
+                       pl.C, pl.Lpad, tei, gates, map, cnt);
+  else
+    hipLaunchKernelGGL((k1_route_map<G, false>), dim3(pl.C), dim3(256), 0, s, logits, L, E, K, pl.T,
+                       pl.C, pl.Lpad, tei, gates, map, cnt);
+}
+
+hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, const float* logits,
+                           int32_t* eti, int32_t* offsets, int32_t* tei, int32_t* tim,
+                           float* gates, char* ws, hipStream_t s) {
+  uint8_t* map = reinterpret_cast<uint8_t*>(ws + pl.off_map);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + pl.off_cnt);
+  int32_t* base = reinterpret_cast<int32_t*>(ws + pl.off_base);
+  int32_t* total = reinterpret_cast<int32_t*>(ws + pl.off_total);
+  {
+    LaunchTimer lt("dispatch_route_map", s);
+    const int q = (E + 3) / 4;  // lanes needed per token
+    if (q <= 1) launch_k1<1>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else if (q <= 2) launch_k1<2>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else if (q <= 4) launch_k1<4>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else if (q <= 8) launch_k1<8>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else if (q <= 16) launch_k1<16>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else if (q <= 32) launch_k1<32>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    else launch_k1<64>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+  }
+  {
+    LaunchTimer lt("dispatch_expert_scan", s);
+    launch_seg_scan(cnt, E, pl.C, 0, base, total, s);
+  }
+  {
+    LaunchTimer lt("dispatch_scatter", s);
+    hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
+                       base, total, eti, offsets, tim);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
