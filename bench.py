@@ -112,8 +112,8 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
 
     n = min(256, cfg.L)
     t = run(n)
-    while t < budget_s / 4 and n < cfg.L:
-        n = min(cfg.L, max(n * 2, int(n * budget_s / max(t, 1e-3) / 2)))
+    while t < budget_s / 2 and n < cfg.L:     # grow the sample to ~budget_s
+        n = min(cfg.L, max(n * 2, int(n * budget_s / max(t, 1e-3))))
         t = run(n)
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} tokens of the workload (same d, h, E, K, weights), "
