@@ -30,6 +30,92 @@ namespace moe {
 // 4j .. 4j+3.  The K winners are found by K rounds of a group arg-max (ties
 // to the lower expert id); the softmax and the ascending-expert slot order
 // come from group reductions and a group prefix count.
+template <int G>
+__device__ __forceinline__ void route_token(const float (&v)[4], int lg, int E, int K, int64_t t,
+                                            int tl, int T, int32_t* __restrict__ tei,
+                                            float* __restrict__ gates, uint8_t* smap) {
+  int ev[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ev[j] = lg * 4 + j;
+  unsigned sel = 0;
+  float vmax = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int be = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool cand = !((sel >> j) & 1u) && ev[j] < E;
+      if (cand && (v[j] > bv || (v[j] == bv && ev[j] < be))) {
+        bv = v[j];
+        be = ev[j];
+      }
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, G);
+      const int oe = __shfl_xor(be, o, G);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (k == 0) vmax = bv;
+    if ((be >> 2) == lg) sel |= 1u << (be & 3);
+  }
+  float ssum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if ((sel >> j) & 1u) ssum += expf(v[j] - vmax);
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) ssum += __shfl_xor(ssum, o, G);
+  const int c = __popc(sel);
+  int inc = c;
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) {
+    const int u = __shfl_up(inc, o, G);
+    if (lg >= o) inc += u;
+  }
+  int slot = inc - c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if ((sel >> j) & 1u) {
+      tei[t * K + slot] = ev[j];
+      gates[t * K + slot] = expf(v[j] - vmax) / ssum;
+      smap[ev[j] * T + tl] = (uint8_t)(slot + 1);
+      ++slot;
+    }
+  }
+}
+
+// The logits of one token for lane lg of its group (-inf where absent).
+// Loads never branch: a missing token or expert reads a valid address and
+// is replaced by -inf.
+template <bool VEC4>
+__device__ __forceinline__ void load_logits(const float* __restrict__ logits, int64_t t, bool ok,
+                                            int E, int lg, float (&v)[4]) {
+  const float* row = logits + (ok ? t : 0) * E;
+  if (VEC4) {
+    const bool in = ok && lg * 4 < E;
+    const float4 q = *reinterpret_cast<const float4*>(row + (in ? lg * 4 : 0));
+    v[0] = in ? q.x : -INFINITY;
+    v[1] = in ? q.y : -INFINITY;
+    v[2] = in ? q.z : -INFINITY;
+    v[3] = in ? q.w : -INFINITY;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lg * 4 + j;
+      const bool in = ok && e < E;
+      const float q = row[in ? e : 0];
+      v[j] = in ? q : -INFINITY;
+    }
+  }
+}
+
+// One workgroup per tile of T tokens.  The tile's logits are read U token
+// groups at a time, all loads issued before any routing, so that each lane
+// keeps U 16-byte loads in flight.  The map tile [E][T] is built in LDS
+// (dynamic, E*T <= 64 KB) and leaves as 16-byte row stores.
 template <int G, bool VEC4>
 __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ logits, int64_t L,
                                                     int E, int K, int T, int C, int64_t Lpad,
@@ -37,81 +123,30 @@ __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ lo
                                                     float* __restrict__ gates,
                                                     uint8_t* __restrict__ map,
                                                     int32_t* __restrict__ tilecnt) {
-  __shared__ __attribute__((aligned(16))) uint8_t smap[65536];  // [E][T]
+  extern __shared__ uint4 smap_v[];
+  uint8_t* smap = reinterpret_cast<uint8_t*>(smap_v);
   const int tile = blockIdx.x;
   const int64_t t0 = (int64_t)tile * T;
   const int nvec = (E * T) >> 4;
-  for (int i = threadIdx.x; i < nvec; i += 256) reinterpret_cast<uint4*>(smap)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < nvec; i += 256) smap_v[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   const int lg = threadIdx.x & (G - 1);
   constexpr int NG = 256 / G;
-  for (int tl = threadIdx.x / G; tl < T; tl += NG) {
-    const int64_t t = t0 + tl;
-    if (t >= L) break;
-    const float* row = logits + t * E;
-    float v[4];
-    int ev[4];
-    if (VEC4) {
-      float4 q = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (lg * 4 < E) q = *reinterpret_cast<const float4*>(row + lg * 4);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  constexpr int U = 8;
+  for (int b0 = threadIdx.x / G; b0 < T; b0 += NG * U) {
+    float v[U][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ev[j] = lg * 4 + j;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ev[j] = lg * 4 + j;
-        v[j] = ev[j] < E ? row[ev[j]] : -INFINITY;
-      }
+    for (int u = 0; u < U; ++u) {
+      const int tl = b0 + u * NG;
+      const int64_t t = t0 + tl;
+      load_logits<VEC4>(logits, t, tl < T && t < L, E, lg, v[u]);
     }
-    unsigned sel = 0;
-    float vmax = 0.f;
-    for (int k = 0; k < K; ++k) {
-      float bv = -INFINITY;
-      int be = INT_MAX;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool cand = !((sel >> j) & 1u) && ev[j] < E;
-        if (cand && (v[j] > bv || (v[j] == bv && ev[j] < be))) {
-          bv = v[j];
-          be = ev[j];
-        }
-      }
-#pragma unroll
-      for (int o = G / 2; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, G);
-        const int oe = __shfl_xor(be, o, G);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (k == 0) vmax = bv;
-      if ((be >> 2) == lg) sel |= 1u << (be & 3);
-    }
-    float ssum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((sel >> j) & 1u) ssum += expf(v[j] - vmax);
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) ssum += __shfl_xor(ssum, o, G);
-    const int c = __popc(sel);
-    int inc = c;
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) {
-      const int u = __shfl_up(inc, o, G);
-      if (lg >= o) inc += u;
-    }
-    int slot = inc - c;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((sel >> j) & 1u) {
-        tei[t * K + slot] = ev[j];
-        gates[t * K + slot] = expf(v[j] - vmax) / ssum;
-        smap[ev[j] * T + tl] = (uint8_t)(slot + 1);
-        ++slot;
-      }
+    for (int u = 0; u < U; ++u) {
+      const int tl = b0 + u * NG;
+      const int64_t t = t0 + tl;
+      if (tl < T && t < L) route_token<G>(v[u], lg, E, K, t, tl, T, tei, gates, smap);
     }
   }
   __syncthreads();
@@ -121,7 +156,7 @@ __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ lo
   for (int e = wave; e < E; e += 4) {
     int cnt = 0;
     for (int i = lane; i < nv; i += 64) {
-      const uint4 q = *reinterpret_cast<const uint4*>(smap + e * T + i * 16);
+      const uint4 q = smap_v[(e * T >> 4) + i];
       *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = q;
       cnt += nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
     }
@@ -151,6 +186,9 @@ __global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt,
 }
 
 // Step 3: per tile, scan each expert's map row segment and scatter.
+// A row segment is T bytes = T/16 lanes of 16 bytes, so one wavefront
+// covers 64/(T/16) rows per pass; the wavefront issues the loads of U passes
+// before scanning any of them.
 __global__ __launch_bounds__(256) void k3_scatter(const uint8_t* __restrict__ map, int64_t Lpad,
                                                   int E, int K, int T, int C,
                                                   const int32_t* __restrict__ tilebase,
@@ -175,28 +213,44 @@ __global__ __launch_bounds__(256) void k3_scatter(const uint8_t* __restrict__ ma
   const int tile = blockIdx.x;
   const int64_t t0 = (int64_t)tile * T;
   const int lane = tid & 63, wave = tid >> 6;
-  for (int e = wave; e < E; e += 4) {
-    int base = s_off[e] + tilebase[(int64_t)e * C + tile];
-    const uint8_t* row = map + (int64_t)e * Lpad + t0;
-    for (int c0 = 0; c0 < T; c0 += 1024) {
-      const int off = c0 + lane * 16;
-      uint4 q = make_uint4(0, 0, 0, 0);
-      if (off < T) q = *reinterpret_cast<const uint4*>(row + off);
-      const int cnt = nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
-      const int incl = wave_incl_scan(cnt, lane);
-      int pos = base + incl - cnt;
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const int seg = T >> 4;            // lanes per row (16, 32 or 64)
+  const int rpw = 64 / seg;          // rows per wavefront pass
+  const int sub = lane / seg, sl = lane % seg;
+  constexpr int U = 4;
+  for (int e0 = wave * rpw; e0 < E; e0 += 4 * rpw * U) {
+    uint4 q[U];
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const uint32_t val = (w[b >> 2] >> ((b & 3) * 8)) & 0xffu;
-        if (val) {
-          const int64_t t = t0 + off + b;
-          eti[pos] = (int32_t)t;
-          tim[t * K + (val - 1)] = pos;
-          ++pos;
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * 4 * rpw + sub;
+      const bool ok = e < E;
+      const uint4 w = *reinterpret_cast<const uint4*>(map + (int64_t)(ok ? e : 0) * Lpad + t0 +
+                                                      sl * 16);
+      q[u] = ok ? w : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * 4 * rpw + sub;
+      const int cnt = nonzero_bytes(q[u].x) + nonzero_bytes(q[u].y) + nonzero_bytes(q[u].z) +
+                      nonzero_bytes(q[u].w);
+      int incl = cnt;
+      for (int o = 1; o < seg; o <<= 1) {
+        const int x = __shfl_up(incl, o, seg);
+        if (sl >= o) incl += x;
+      }
+      if (e < E && cnt > 0) {
+        int pos = s_off[e] + tilebase[(int64_t)e * C + tile] + incl - cnt;
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const uint32_t val = (w[b >> 2] >> ((b & 3) * 8)) & 0xffu;
+          if (val) {
+            const int64_t t = t0 + sl * 16 + b;
+            eti[pos] = (int32_t)t;
+            tim[t * K + (val - 1)] = pos;
+            ++pos;
+          }
         }
       }
-      base += __shfl(incl, 63, 64);
     }
   }
 }
@@ -209,7 +263,7 @@ void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, in
 DispatchPlan plan_dispatch(int64_t L, int E, int K) {
   (void)K;
   DispatchPlan p;
-  int T = (65536 / E) / 256 * 256;
+  int T = (32768 / E) / 256 * 256;
   if (T > 1024) T = 1024;
   if (T < 256) T = 256;
   p.T = T;
@@ -229,11 +283,11 @@ static void launch_k1(const DispatchPlan& pl, int64_t L, int E, int K, const flo
                       int32_t* tei, float* gates, uint8_t* map, int32_t* cnt, hipStream_t s) {
   const bool vec4 = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   if (vec4)
-    hipLaunchKernelGGL((k1_route_map<G, true>), dim3(pl.C), dim3(256), 0, s, logits, L, E, K, pl.T,
-                       pl.C, pl.Lpad, tei, gates, map, cnt);
+    hipLaunchKernelGGL((k1_route_map<G, true>), dim3(pl.C), dim3(256), (size_t)E * pl.T, s, logits,
+                       L, E, K, pl.T, pl.C, pl.Lpad, tei, gates, map, cnt);
   else
-    hipLaunchKernelGGL((k1_route_map<G, false>), dim3(pl.C), dim3(256), 0, s, logits, L, E, K, pl.T,
-                       pl.C, pl.Lpad, tei, gates, map, cnt);
+    hipLaunchKernelGGL((k1_route_map<G, false>), dim3(pl.C), dim3(256), (size_t)E * pl.T, s,
+                       logits, L, E, K, pl.T, pl.C, pl.Lpad, tei, gates, map, cnt);
 }
 
 hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, const float* logits,

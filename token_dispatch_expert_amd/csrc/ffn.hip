@@ -15,17 +15,24 @@
 //     input gradients of both branches are summed inside one GEMM over the
 //     concatenated [dA | dB] x [W1 | W3]^T.
 //
-// GEMM engine (all six GEMMs): 128 x 128 output tile per 256-thread
-// workgroup, four wavefronts in a 2 x 2 grid, each wavefront 2 x 2 MFMA
-// 32x32 tiles (bf16: v_mfma_f32_32x32x16_bf16; float32: four
-// v_mfma_f32_32x32x2f32 per 8-element k group).  One k-tile is 128 bytes of
-// k per row (64 bf16 / 32 float32); both operands are staged in LDS with k
-// contiguous per row, double buffered, with the next k-tile's global loads
-// issued before the current tile's MFMAs.  Operands whose memory layout has
-// k contiguous are copied with 16-byte loads; operands with the M/N index
-// contiguous (weights in x W, and both sides of the weight-gradient
-// products) are loaded as 4 (k) x 16-byte blocks and transposed in
-// registers on the way into LDS.
+// GEMM engine (all six GEMMs): a 256 x 256 output tile per 512-thread
+// workgroup; eight wavefronts (two per SIMD) in a 2 x 4 grid, each owning
+// 128 x 64 = 4 x 2 MFMA 32x32 tiles (bf16: v_mfma_f32_32x32x16_bf16;
+// float32: four v_mfma_f32_32x32x2f32 per 8-element k group).  One k-tile is
+// 128 bytes of k per row (64 bf16 / 32 float32).  Both operands sit in LDS
+// with k contiguous per row; the eight 16-byte chunks of a row are XOR-
+// swizzled by the row index so that fragment reads, row copies and the
+// transposed writes below do not collide on banks.  LDS is double buffered
+// (128 KB) and the next k-tile's global loads are issued before the current
+// tile's MFMAs.  Loads never branch: out-of-range rows or k read a valid
+// address and are zeroed by a select.
+//
+// Operand layouts.  The forward products use weights transposed once per
+// call into the workspace (W1, W3 -> [E, h, d]; W2 -> [E, d, h]), so every
+// operand of F1, F2, B1 and B3 has k contiguous and is copied with 16-byte
+// row loads.  The weight-gradient products B0 and B2 reduce over routes, so
+// both of their operands have the M/N index contiguous; those are loaded as
+// 4 k-rows x 16 bytes and transposed in registers on the way into LDS.
 //
 // Determinism: every output element has one writer.  The combine into y
 // and the input gradient dx run as K ordered slot passes: pass k handles,
@@ -38,14 +45,14 @@
 
 namespace moe {
 
-constexpr int NT = 256;        // threads per workgroup
-constexpr int TBM = 128;       // output tile rows
-constexpr int TBN = 128;       // output tile columns (logical)
-constexpr int ROWB = 128;      // bytes of k per LDS row per k-tile
-constexpr int PITCH = ROWB + 16;
-constexpr int OPB = 128 * PITCH;         // one operand tile in LDS
+constexpr int NT = 512;                  // threads per workgroup
+constexpr int TBM = 256;                 // output tile rows
+constexpr int TBN = 256;                 // output tile columns (logical)
+constexpr int ROWB = 128;                // bytes of k per LDS row per k-tile
+constexpr int OPB = 256 * ROWB;          // one operand tile in LDS (32 KB)
 constexpr int STAGE = 2 * OPB;           // A + B
-constexpr int LDSB = 2 * STAGE;          // double buffered
+constexpr int LDSB = 2 * STAGE;          // double buffered (128 KB)
+constexpr int MT = 4, NTL = 2;           // MFMA 32x32 tiles per wavefront (M, N)
 
 template <typename T> struct Traits;
 template <> struct Traits<bf16_t> {
@@ -55,6 +62,11 @@ template <> struct Traits<float> {
   static constexpr int ES = 4, VEC = 4, KT = 32;
 };
 
+// Byte offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * ROWB + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   // Workgroups are handed out round-robin over the 8 XCDs; give each XCD a
   // contiguous run of logical tiles so neighbouring tiles share its L2.
@@ -62,103 +74,182 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+__device__ __forceinline__ uint4 sel16(bool ok, uint4 v) {
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
 // ------------------------------------------------------------------ loaders
 
-// Tile of 128 rows with k contiguous in memory.  Thread owns rows
-// (tid >> 3) + 32 i (i < 4) and the 16-byte column (tid & 7) of each k-tile.
-// Elements k < ksplit come from p0[i] + k, the rest from p1[i] + (k - ksplit).
+// 256 rows with k contiguous in memory.  Thread owns rows (tid >> 3) + 64 i
+// (i < 4) and 16-byte chunk (tid & 7) of each k-tile.  Element k of row i is
+// at p0[i] + k (k < ksplit) or p0[i] + delta + (k - ksplit) (k >= ksplit):
+// the second source has the same row layout at a fixed byte distance.
+// Rows that are out of range point at a valid row and are zeroed.
 template <typename T>
 struct KLoader {
   const char* p0[4];
-  const char* p1[4];
+  uint32_t valid;
+  int64_t delta;
   int ksplit, klen;
   uint4 reg[4];
 
   __device__ __forceinline__ void fetch(int kt) {
     constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
     const int k = kt * KT + (threadIdx.x & 7) * VEC;
+    const bool inK = k < klen;
+    const int64_t o = !inK ? 0 : (k < ksplit ? (int64_t)k * ES : delta + (int64_t)(k - ksplit) * ES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p0[i] != nullptr && k < klen) {
-        const char* p = k < ksplit ? p0[i] + (int64_t)k * ES : p1[i] + (int64_t)(k - ksplit) * ES;
-        v = *reinterpret_cast<const uint4*>(p);
-      }
-      reg[i] = v;
-    }
+    for (int i = 0; i < 4; ++i)
+      reg[i] = sel16(inK && ((valid >> i) & 1u), *reinterpret_cast<const uint4*>(p0[i] + o));
   }
   __device__ __forceinline__ void store(char* lds) const {
-    const int r = threadIdx.x >> 3, c = (threadIdx.x & 7) * 16;
+    const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + (r + 32 * i) * PITCH + c) = reg[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + lds_off(r + 64 * i, c)) = reg[i];
   }
 };
 
-// Tile of 128 M/N positions with that index contiguous in memory and k
-// indexing rows.  Thread owns k rows kt*KT + kb*4 + i (i < 4) and one
-// 16-byte vector of VEC positions starting at logical position nb*VEC.
-// Row r(k) = ridx ? ridx[k] : rbase + k; the element sits at col + r * ld.
+// Row pointers of a KLoader: LDS row j of the tile is list entry rb + j
+// (the identity list when list == nullptr), optionally mapped through
+// `gather`; row index idx lives at base + idx * row_elems.  Entries at or
+// past `re` are invalid.
+template <typename T>
+__device__ __forceinline__ void kloader_rows(KLoader<T>& la, const T* base, const int32_t* list,
+                                             const int32_t* gather, int rb, int re,
+                                             int64_t row_elems) {
+  const int r = threadIdx.x >> 3;
+  la.valid = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int li = rb + r + 64 * i;
+    const bool ok = li < re;
+    int64_t idx = 0;
+    if (ok) {
+      idx = list != nullptr ? (int64_t)list[li] : (int64_t)li;
+      if (gather != nullptr) idx = gather[idx];
+    }
+    la.p0[i] = reinterpret_cast<const char*>(base + idx * row_elems);
+    la.valid |= (ok ? 1u : 0u) << i;
+  }
+}
+
+// 256 M/N positions with that index contiguous in memory, k indexing rows.
+// Row r(k) = ridx ? ridx[k] : rbase + k; the thread's 16-byte vector for
+// k-row k is at col + r(k) * ld.
+//   bf16:    thread t owns positions (t >> 4) * 8 .. +8 and k-rows
+//            ((t >> 1) & 7) * 8 + (t & 1) * 4 + i, i < 4 (half of a 16-byte
+//            k chunk); it writes 8 position rows x 8 bytes.
+//   float32: thread t owns positions (t >> 3) * 4 .. +4 and k-rows
+//            (t & 7) * 4 + i, i < 4 (a whole chunk); it writes 4 rows x 16 B.
+// Odd position groups write their rows in pair-swapped order so that
+// consecutive lanes cover both row parities of an LDS cycle.
 template <typename T>
 struct MNLoader {
   const char* col;
-  int64_t ld;            // bytes
+  bool colok;
+  int64_t ld;
   const int32_t* ridx;
   int64_t rbase;
   int klen;
+  int64_t rnext[4];
   uint4 reg[4];
 
-  static constexpr int NV = 128 / Traits<T>::VEC;
-  __device__ static __forceinline__ int nb() { return threadIdx.x % NV; }
-  __device__ static __forceinline__ int kb() { return threadIdx.x / NV; }
+  __device__ static __forceinline__ int pos0();     // first position of the thread
+  __device__ static __forceinline__ int krow0();    // first k-row of the thread in a tile
 
-  __device__ __forceinline__ void fetch(int kt) {
+  // Positions first_pos + pos0() .. of `base` (an array with `limit`
+  // positions per row and ld bytes between rows).
+  __device__ __forceinline__ void setup(const char* base, int first_pos, int limit, int64_t ld_,
+                                        const int32_t* ridx_, int64_t rbase_, int klen_) {
+    constexpr int ES = Traits<T>::ES;
+    const int p = first_pos + pos0();
+    colok = p < limit;
+    col = base + (int64_t)(colok ? p : 0) * ES;
+    ld = ld_;
+    ridx = ridx_;
+    rbase = rbase_;
+    klen = klen_;
+    prime();
+  }
+  // Row indices of k-tile kt (gathered rows: loaded one k-tile ahead so that
+  // the index load never sits in front of the data load).
+  __device__ __forceinline__ void rows_of(int kt, int64_t (&rr)[4]) const {
     constexpr int KT = Traits<T>::KT;
-    const int k0 = kt * KT + kb() * 4;
+    const int k0 = kt * KT + krow0();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col != nullptr && k < klen) {
-        const int64_t r = ridx != nullptr ? (int64_t)ridx[k] : rbase + k;
-        v = *reinterpret_cast<const uint4*>(col + r * ld);
-      }
-      reg[i] = v;
+      const int kk = (colok && k < klen) ? k : 0;
+      rr[i] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
+    }
+  }
+  __device__ __forceinline__ void prime() { rows_of(0, rnext); }
+  __device__ __forceinline__ void fetch(int kt) {
+    constexpr int KT = Traits<T>::KT;
+    const int k0 = kt * KT + krow0();
+    int64_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = rnext[i];
+    rows_of(kt + 1, rnext);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = colok && k0 + i < klen;
+      reg[i] = sel16(ok, *reinterpret_cast<const uint4*>(col + r[i] * ld));
     }
   }
   __device__ __forceinline__ void store(char* lds) const;
 };
 
 template <>
+__device__ __forceinline__ int MNLoader<bf16_t>::pos0() { return (threadIdx.x >> 4) * 8; }
+template <>
+__device__ __forceinline__ int MNLoader<bf16_t>::krow0() {
+  return ((threadIdx.x >> 1) & 7) * 8 + (threadIdx.x & 1) * 4;
+}
+template <>
+__device__ __forceinline__ int MNLoader<float>::pos0() { return (threadIdx.x >> 3) * 4; }
+template <>
+__device__ __forceinline__ int MNLoader<float>::krow0() { return (threadIdx.x & 7) * 4; }
+
+template <>
 __device__ __forceinline__ void MNLoader<bf16_t>::store(char* lds) const {
-  const int n0 = nb() * 8;
-  const int kbyte = kb() * 8;
+  const int c = (threadIdx.x >> 1) & 7, half = (threadIdx.x & 1) * 8;
+  const int n0 = pos0(), odd = (threadIdx.x >> 4) & 1;
   const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&reg[0]);
   const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&reg[1]);
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&reg[2]);
   const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&reg[3]);
+  uint2 out[8];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint2 lo, hi;
-    lo.x = (q0[w] & 0xffffu) | (q1[w] << 16);
-    lo.y = (q2[w] & 0xffffu) | (q3[w] << 16);
-    hi.x = (q0[w] >> 16) | (q1[w] & 0xffff0000u);
-    hi.y = (q2[w] >> 16) | (q3[w] & 0xffff0000u);
-    *reinterpret_cast<uint2*>(lds + (n0 + 2 * w) * PITCH + kbyte) = lo;
-    *reinterpret_cast<uint2*>(lds + (n0 + 2 * w + 1) * PITCH + kbyte) = hi;
+    out[2 * w].x = (q0[w] & 0xffffu) | (q1[w] << 16);
+    out[2 * w].y = (q2[w] & 0xffffu) | (q3[w] << 16);
+    out[2 * w + 1].x = (q0[w] >> 16) | (q1[w] & 0xffff0000u);
+    out[2 * w + 1].y = (q2[w] >> 16) | (q3[w] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint2 v = odd ? out[j ^ 1] : out[j];
+    *reinterpret_cast<uint2*>(lds + lds_off(n0 + (j ^ odd), c) + half) = v;
   }
 }
 
 template <>
 __device__ __forceinline__ void MNLoader<float>::store(char* lds) const {
-  const int n0 = nb() * 4;
-  const int kbyte = kb() * 16;
+  const int c = threadIdx.x & 7;
+  const int n0 = pos0(), odd = (threadIdx.x >> 3) & 1;
   const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&reg[0]);
   const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&reg[1]);
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&reg[2]);
   const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&reg[3]);
+  uint4 out[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<uint4*>(lds + (n0 + c) * PITCH + kbyte) = make_uint4(q0[c], q1[c], q2[c], q3[c]);
+  for (int j = 0; j < 4; ++j) out[j] = make_uint4(q0[j], q1[j], q2[j], q3[j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 v = odd ? out[j ^ 1] : out[j];
+    *reinterpret_cast<uint4*>(lds + lds_off(n0 + (j ^ odd), c)) = v;
+  }
 }
 
 // ------------------------------------------------------------------ MFMA
@@ -185,27 +276,30 @@ __device__ __forceinline__ f32x16_t mfma_k8<float>(uint4 a, uint4 b, f32x16_t c)
 }
 
 struct Acc {
-  f32x16_t c[2][2];
+  f32x16_t c[MT][NTL];
 };
+
+__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) >> 2; }
+__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) & 3; }
 
 template <typename T>
 __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& acc) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave_m(), wn = wave_n();
   const int r = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    uint4 a[2], b[2];
+    uint4 a[MT], b[NTL];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      a[mt] = *reinterpret_cast<const uint4*>(As + (wm * 64 + mt * 32 + r) * PITCH + kc * 32 + g * 16);
+    for (int mt = 0; mt < MT; ++mt)
+      a[mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, kc * 2 + g));
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      b[nt] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + nt * 32 + r) * PITCH + kc * 32 + g * 16);
+    for (int nt = 0; nt < NTL; ++nt)
+      b[nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, kc * 2 + g));
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[mt], b[nt], acc.c[mt][nt]);
+      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[mt], b[nt], acc.c[mt][nt]);
   }
 }
 
@@ -213,9 +307,9 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc.c[mt][nt][i] = 0.f;
   if (nk <= 0) return;
@@ -242,17 +336,19 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 }
 
 // Position of accumulator element i of MFMA tile (mt, nt) inside the
-// 128 x 128 workgroup tile.
+// 256 x 256 workgroup tile.
 __device__ __forceinline__ int acc_row(int mt, int i) {
-  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-  return wm * 64 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+  const int lane = threadIdx.x & 63;
+  return wave_m() * 128 + mt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
 }
 __device__ __forceinline__ int acc_col(int nt) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-  return wn * 64 + nt * 32 + (lane & 31);
+  const int lane = threadIdx.x & 63;
+  return wave_n() * 64 + nt * 32 + (lane & 31);
 }
-// For interleaved dual-B tiles (two matrices, 64 columns each per tile):
-// logical column -> (matrix, column within the 64-wide source range).
+// Interleaved dual-B tiles (two matrices, 128 columns of each per tile):
+// logical column lc -> matrix (lc >> 5) & 1, source column (lc >> 6) * 32 +
+// (lc & 31).  A wavefront's accumulator tile 0 then holds matrix 0 and tile
+// 1 holds matrix 1 at the same source column.
 __device__ __forceinline__ int dual_src(int lc) { return (lc >> 5) & 1; }
 __device__ __forceinline__ int dual_col(int lc) { return (lc >> 6) * 32 + (lc & 31); }
 
@@ -268,6 +364,28 @@ template <>
 __device__ __forceinline__ float sigm_of<bf16_t>(float a) { return 1.0f / (1.0f + __expf(-a)); }
 template <>
 __device__ __forceinline__ float sigm_of<float>(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+// ------------------------------------------------------------------ weights
+
+// WT[e][c][r] = W[e][r][c] for an [E][R][C] tensor (64 x 64 tiles via LDS).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_weights(const T* __restrict__ W,
+                                                         T* __restrict__ WT, int R, int C) {
+  __shared__ float tile[64][65];
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const T* src = W + (int64_t)e * R * C;
+  T* dst = WT + (int64_t)e * R * C;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63;
+    if (r0 + r < R && c0 + c < C) tile[r][c] = Elem<T>::load(src + (int64_t)(r0 + r) * C + c0 + c);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i >> 6, r = i & 63;
+    if (r0 + r < R && c0 + c < C) Elem<T>::store(dst + (int64_t)(c0 + c) * R + r0 + r, tile[r][c]);
+  }
+}
 
 // ------------------------------------------------------------------ tiles
 
@@ -395,55 +513,60 @@ struct RouteArgs {            // row tiles over routes or slot-pass lists
   int nN;                     // column tiles
 };
 
-// F1: [A | B] = X W1 [| X W3] with X gathered by expert_token_indices;
-// epilogue writes A, B (checkpoint) and G = SiLU(A) [* B].
-template <typename T, bool DUAL>
-__global__ __launch_bounds__(NT) void f1_gather_glu(RouteArgs ra, const T* __restrict__ x,
-                                                    const T* __restrict__ W1,
-                                                    const T* __restrict__ W3,
-                                                    const int32_t* __restrict__ eti, int d, int h,
-                                                    T* __restrict__ A, T* __restrict__ B,
-                                                    T* __restrict__ G) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
+// Tile coordinates of a route-major GEMM workgroup; false if it has no work.
+__device__ __forceinline__ bool route_tile(const RouteArgs& ra, int4& ds, int& ntile) {
   const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t mtile = lid / ra.nN;
-  const int ntile = (int)(lid % ra.nN);
-  if (mtile >= ra.ntiles) return;
-  const int4 ds = ra.tiles[mtile];
-  if (ds.x < 0) return;
+  ntile = (int)(lid % ra.nN);
+  if (mtile >= ra.ntiles) return false;
+  ds = ra.tiles[mtile];
+  return ds.x >= 0;
+}
+
+// F1: [A | B] = X W1 [| X W3] with X gathered by expert_token_indices;
+// epilogue writes A, B (checkpoint) and G = SiLU(A) [* B].
+// W1T, W3T: [E, h, d] (transposed weights).
+template <typename T, bool DUAL>
+__global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __restrict__ x,
+                                                       const T* __restrict__ W1T,
+                                                       const T* __restrict__ W3T,
+                                                       const int32_t* __restrict__ eti, int d,
+                                                       int h, T* __restrict__ A,
+                                                       T* __restrict__ B, T* __restrict__ G) {
+  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  constexpr int KT = Traits<T>::KT;
+  int4 ds;
+  int ntile;
+  if (!route_tile(ra, ds, ntile)) return;
   const int e = ds.x, rb = ds.y, re = ds.z;
-  const int n0 = ntile * (DUAL ? 64 : 128);
+  const int n0 = ntile * (DUAL ? 128 : 256);
 
   KLoader<T> la;
+  kloader_rows<T>(la, x, nullptr, eti, rb, re, d);
+  la.delta = 0;
+  la.ksplit = la.klen = d;
+  KLoader<T> lb;
   {
     const int r = threadIdx.x >> 3;
+    lb.valid = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = rb + r + 32 * i;
-      la.p0[i] = p < re ? reinterpret_cast<const char*>(x + (int64_t)eti[p] * d) : nullptr;
-      la.p1[i] = la.p0[i];
+      const int lr = r + 64 * i;
+      const int src = DUAL ? dual_src(lr) : 0;
+      const int sc = n0 + (DUAL ? dual_col(lr) : lr);
+      const bool ok = sc < h;
+      const T* Wm = (src == 0 ? W1T : W3T) + ((int64_t)e * h + (ok ? sc : 0)) * d;
+      lb.p0[i] = reinterpret_cast<const char*>(Wm);
+      lb.valid |= (ok ? 1u : 0u) << i;
     }
-    la.ksplit = d;
-    la.klen = d;
-  }
-  MNLoader<T> lb;
-  {
-    const int lc = MNLoader<T>::nb() * VEC;
-    const int src = DUAL ? dual_src(lc) : 0;
-    const int sc = n0 + (DUAL ? dual_col(lc) : lc);
-    const T* W = (src == 0 ? W1 : W3) + (int64_t)e * d * h;
-    lb.col = sc < h ? reinterpret_cast<const char*>(W + sc) : nullptr;
-    lb.ld = (int64_t)h * ES;
-    lb.ridx = nullptr;
-    lb.rbase = 0;
-    lb.klen = d;
+    lb.delta = 0;
+    lb.ksplit = lb.klen = d;
   }
   Acc acc;
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
 
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = rb + acc_row(mt, i);
@@ -459,7 +582,7 @@ __global__ __launch_bounds__(NT) void f1_gather_glu(RouteArgs ra, const T* __res
         }
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTL; ++nt) {
           const int c = n0 + acc_col(nt);
           if (c < h) {
             const float a = acc.c[mt][nt][i];
@@ -473,139 +596,166 @@ __global__ __launch_bounds__(NT) void f1_gather_glu(RouteArgs ra, const T* __res
   }
 }
 
-// Accumulate one slot pass into the (L, d) output.
+// Slot-pass epilogue: out/acc row t = s_t[row] (-1: no row), scale s_g[row].
 //   mode 0: only pass (K == 1): out = v
 //   mode 1: first pass:  acc = v
 //   mode 2: middle pass: acc += v
 //   mode 3: last pass:   out = acc + v
-// For float32 outputs `acc` is the output itself (modes 1/2 only).
+// For float32 outputs `acc` is the output itself (modes 1/2 only).  The
+// accumulator values of one MFMA row block are all loaded before any is
+// used, from a valid address when the element is absent.
 template <typename T>
-__device__ __forceinline__ void combine_store(T* out, float* acc, int64_t o, float v, int mode) {
-  if (mode == 0) Elem<T>::store(out + o, v);
-  else if (mode == 1) acc[o] = v;
-  else if (mode == 2) acc[o] += v;
-  else Elem<T>::store(out + o, acc[o] + v);
-}
-
-// F2 (slot pass k): O = G W2_e for the pass's rows, y[t] (+)= gate * O.
-template <typename T>
-__global__ __launch_bounds__(NT) void f2_down_combine(RouteArgs ra, const T* __restrict__ Gb,
-                                                      const T* __restrict__ W2,
-                                                      const int32_t* __restrict__ list,
-                                                      const int32_t* __restrict__ eti,
-                                                      const float* __restrict__ gates, int K,
-                                                      int k, int d, int h, int mode,
-                                                      T* __restrict__ y, float* __restrict__ yacc) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mtile = lid / ra.nN;
-  const int ntile = (int)(lid % ra.nN);
-  if (mtile >= ra.ntiles) return;
-  const int4 ds = ra.tiles[mtile];
-  if (ds.x < 0) return;
-  const int e = ds.x, rb = ds.y, re = ds.z;
-  const int n0 = ntile * 128;
-
-  KLoader<T> la;
-  {
-    const int r = threadIdx.x >> 3;
+__device__ __forceinline__ void combine_epilogue(const Acc& acc, const int64_t* s_t,
+                                                 const float* s_g, int n0, int d, int mode,
+                                                 T* __restrict__ out, float* __restrict__ accb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int li = rb + r + 32 * i;
-      la.p0[i] = li < re ? reinterpret_cast<const char*>(Gb + (int64_t)list[li] * h) : nullptr;
-      la.p1[i] = la.p0[i];
+  for (int mt = 0; mt < MT; ++mt) {
+    float prev[16][NTL];
+    if (mode >= 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t t = s_t[acc_row(mt, i)];
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+          const int c = n0 + acc_col(nt);
+          const bool ok = t >= 0 && c < d;
+          const float x = accb[ok ? t * d + c : 0];
+          prev[i][nt] = ok ? x : 0.f;
+        }
+      }
     }
-    la.ksplit = h;
-    la.klen = h;
-  }
-  MNLoader<T> lb;
-  {
-    const int sc = n0 + MNLoader<T>::nb() * VEC;
-    lb.col = sc < d ? reinterpret_cast<const char*>(W2 + (int64_t)e * h * d + sc) : nullptr;
-    lb.ld = (int64_t)d * ES;
-    lb.ridx = nullptr;
-    lb.rbase = 0;
-    lb.klen = h;
-  }
-  Acc acc;
-  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
-
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int li = rb + acc_row(mt, i);
-      if (li >= re) continue;
-      const int64_t t = eti[list[li]];
-      const float g = gates[t * K + k];
+      const int row = acc_row(mt, i);
+      const int64_t t = s_t[row];
+      const float g = s_g[row];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTL; ++nt) {
         const int c = n0 + acc_col(nt);
-        if (c < d) combine_store<T>(y, yacc, t * d + c, g * acc.c[mt][nt][i], mode);
+        if (t < 0 || c >= d) continue;
+        const int64_t o = t * d + c;
+        const float v = g * acc.c[mt][nt][i];
+        if (mode == 0) Elem<T>::store(out + o, v);
+        else if (mode == 1) accb[o] = v;
+        else if (mode == 2) accb[o] = prev[i][nt] + v;
+        else Elem<T>::store(out + o, prev[i][nt] + v);
       }
     }
   }
 }
 
+// F2 (slot pass k): O = G W2_e for the pass's rows, y[t] (+)= gate * O.
+// W2T: [E, d, h] (transposed weights).
+template <typename T>
+__global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* __restrict__ Gb,
+                                                         const T* __restrict__ W2T,
+                                                         const int32_t* __restrict__ list,
+                                                         const int32_t* __restrict__ eti,
+                                                         const float* __restrict__ gates, int K,
+                                                         int k, int d, int h, int mode,
+                                                         T* __restrict__ y,
+                                                         float* __restrict__ yacc) {
+  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ int64_t s_t[TBM];
+  __shared__ float s_g[TBM];
+  constexpr int KT = Traits<T>::KT;
+  int4 ds;
+  int ntile;
+  if (!route_tile(ra, ds, ntile)) return;
+  const int e = ds.x, rb = ds.y, re = ds.z;
+  const int n0 = ntile * 256;
+  if (threadIdx.x < TBM) {
+    const int li = rb + threadIdx.x;
+    int64_t t = -1;
+    float g = 0.f;
+    if (li < re) {
+      t = eti[list[li]];
+      g = gates[t * K + k];
+    }
+    s_t[threadIdx.x] = t;
+    s_g[threadIdx.x] = g;
+  }
+
+  KLoader<T> la;
+  kloader_rows<T>(la, Gb, list, nullptr, rb, re, h);
+  la.delta = 0;
+  la.ksplit = la.klen = h;
+  KLoader<T> lb;
+  kloader_rows<T>(lb, W2T + (int64_t)e * d * h, nullptr, nullptr, n0, d, h);
+  lb.delta = 0;
+  lb.ksplit = lb.klen = h;
+  Acc acc;
+  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
+  __syncthreads();
+  combine_epilogue<T>(acc, s_t, s_g, n0, d, mode, y, yacc);
+}
+
 // B1: dG = gate * (dy[t] W2_e^T) per route; epilogue recomputes SiLU from
 // the checkpoint and writes dA, dB over A, B and Gs = gate * G.
 template <typename T, bool DUAL>
-__global__ __launch_bounds__(NT) void b1_dgrad_glu(RouteArgs ra, const T* __restrict__ dy,
-                                                   const T* __restrict__ W2,
-                                                   const int32_t* __restrict__ eti,
-                                                   const float* __restrict__ gate_p, int d, int h,
-                                                   T* __restrict__ A, T* __restrict__ B,
-                                                   T* __restrict__ Gs) {
+__global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __restrict__ dy,
+                                                      const T* __restrict__ W2,
+                                                      const int32_t* __restrict__ eti,
+                                                      const float* __restrict__ gate_p, int d,
+                                                      int h, T* __restrict__ A,
+                                                      T* __restrict__ B, T* __restrict__ Gs) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mtile = lid / ra.nN;
-  const int ntile = (int)(lid % ra.nN);
-  if (mtile >= ra.ntiles) return;
-  const int4 ds = ra.tiles[mtile];
-  if (ds.x < 0) return;
+  int4 ds;
+  int ntile;
+  if (!route_tile(ra, ds, ntile)) return;
   const int e = ds.x, rb = ds.y, re = ds.z;
-  const int n0 = ntile * 128;
+  const int n0 = ntile * 256;
+  if (threadIdx.x < TBM) {
+    const int p = rb + threadIdx.x;
+    s_g[threadIdx.x] = p < re ? gate_p[p] : 0.f;
+  }
 
   KLoader<T> la;
+  kloader_rows<T>(la, dy, nullptr, eti, rb, re, d);
+  la.delta = 0;
+  la.ksplit = la.klen = d;
   KLoader<T> lb;
-  {
-    const int r = threadIdx.x >> 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = rb + r + 32 * i;
-      la.p0[i] = p < re ? reinterpret_cast<const char*>(dy + (int64_t)eti[p] * d) : nullptr;
-      la.p1[i] = la.p0[i];
-      const int n = n0 + r + 32 * i;
-      lb.p0[i] = n < h ? reinterpret_cast<const char*>(W2 + ((int64_t)e * h + n) * d) : nullptr;
-      lb.p1[i] = lb.p0[i];
-    }
-    la.ksplit = la.klen = d;
-    lb.ksplit = lb.klen = d;
-  }
+  kloader_rows<T>(lb, W2 + (int64_t)e * h * d, nullptr, nullptr, n0, h, d);
+  lb.delta = 0;
+  lb.ksplit = lb.klen = d;
   Acc acc;
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
+  __syncthreads();
 
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
+    float av[16][NTL], bv[16][NTL];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = rb + acc_row(mt, i);
-      if (p >= re) continue;
-      const float gp = gate_p[p];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTL; ++nt) {
         const int c = n0 + acc_col(nt);
-        if (c >= h) continue;
+        const bool ok = p < re && c < h;
+        const int64_t o = ok ? (int64_t)p * h + c : 0;
+        av[i][nt] = Elem<T>::load(A + o);
+        bv[i][nt] = DUAL ? Elem<T>::load(B + o) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(mt, i);
+      const int p = rb + row;
+      const float gp = s_g[row];
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) {
+        const int c = n0 + acc_col(nt);
+        if (p >= re || c >= h) continue;
         const int64_t o = (int64_t)p * h + c;
         const float dg = gp * acc.c[mt][nt][i];
-        const float a = Elem<T>::load(A + o);
+        const float a = av[i][nt];
         const float s = sigm_of<T>(a);
         const float sl = a * s;
         const float ds_ = s * (1.0f + a * (1.0f - s));
         if (DUAL) {
-          const float b = Elem<T>::load(B + o);
+          const float b = bv[i][nt];
           Elem<T>::store(A + o, dg * b * ds_);
           Elem<T>::store(B + o, dg * sl);
           Elem<T>::store(Gs + o, gp * sl * b);
@@ -622,53 +772,47 @@ struct WeightArgs {           // weight-gradient tiles: E x nM x nN
   int E, nM, nN;
 };
 
-// B0: dW2_e = Gs_e^T dy_e (reduction over the expert's routes, ascending).
-template <typename T>
-__global__ __launch_bounds__(NT) void b0_dw2(WeightArgs wa, const T* __restrict__ Gs,
-                                             const T* __restrict__ dy,
-                                             const int32_t* __restrict__ eti,
-                                             const int32_t* __restrict__ offsets, int d, int h,
-                                             T* __restrict__ dW2) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
+__device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& mi, int& ni) {
   const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t per_e = (int64_t)wa.nM * wa.nN;
-  if (lid >= (int64_t)wa.E * per_e) return;
-  const int e = (int)(lid / per_e);
+  if (lid >= (int64_t)wa.E * per_e) return false;
+  e = (int)(lid / per_e);
   const int rem = (int)(lid % per_e);
-  const int m0 = (rem / wa.nN) * 128, n0 = (rem % wa.nN) * 128;
+  mi = rem / wa.nN;
+  ni = rem % wa.nN;
+  return true;
+}
+
+// B0: dW2_e = Gs_e^T dy_e (reduction over the expert's routes, ascending).
+template <typename T>
+__global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restrict__ Gs,
+                                                const T* __restrict__ dy,
+                                                const int32_t* __restrict__ eti,
+                                                const int32_t* __restrict__ offsets, int d, int h,
+                                                T* __restrict__ dW2) {
+  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
+  int e, mi, ni;
+  if (!weight_tile(wa, e, mi, ni)) return;
+  const int m0 = mi * 256, n0 = ni * 256;
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
   MNLoader<T> la;
-  {
-    const int sc = m0 + MNLoader<T>::nb() * VEC;
-    la.col = sc < h ? reinterpret_cast<const char*>(Gs + sc) : nullptr;
-    la.ld = (int64_t)h * ES;
-    la.ridx = nullptr;
-    la.rbase = o0;
-    la.klen = n_e;
-  }
+  la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
   MNLoader<T> lb;
-  {
-    const int sc = n0 + MNLoader<T>::nb() * VEC;
-    lb.col = sc < d ? reinterpret_cast<const char*>(dy + sc) : nullptr;
-    lb.ld = (int64_t)d * ES;
-    lb.ridx = eti + o0;
-    lb.rbase = 0;
-    lb.klen = n_e;
-  }
+  lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
   Acc acc;
   gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
 
   T* out = dW2 + (int64_t)e * h * d;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = m0 + acc_row(mt, i);
       if (m >= h) continue;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTL; ++nt) {
         const int c = n0 + acc_col(nt);
         if (c < d) Elem<T>::store(out + (int64_t)m * d + c, acc.c[mt][nt][i]);
       }
@@ -678,42 +822,31 @@ __global__ __launch_bounds__(NT) void b0_dw2(WeightArgs wa, const T* __restrict_
 // B2: dW1_e = X_e^T dA_e [, dW3_e = X_e^T dB_e], X gathered by
 // expert_token_indices; both products share the X tile (interleaved columns).
 template <typename T, bool DUAL>
-__global__ __launch_bounds__(NT) void b2_dw13(WeightArgs wa, const T* __restrict__ x,
-                                              const T* __restrict__ dA,
-                                              const T* __restrict__ dB,
-                                              const int32_t* __restrict__ eti,
-                                              const int32_t* __restrict__ offsets, int d, int h,
-                                              T* __restrict__ dW1, T* __restrict__ dW3) {
+__global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restrict__ x,
+                                                 const T* __restrict__ dA,
+                                                 const T* __restrict__ dB,
+                                                 const int32_t* __restrict__ eti,
+                                                 const int32_t* __restrict__ offsets, int d,
+                                                 int h, T* __restrict__ dW1,
+                                                 T* __restrict__ dW3) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t per_e = (int64_t)wa.nM * wa.nN;
-  if (lid >= (int64_t)wa.E * per_e) return;
-  const int e = (int)(lid / per_e);
-  const int rem = (int)(lid % per_e);
-  const int m0 = (rem / wa.nN) * 128, n0 = (rem % wa.nN) * (DUAL ? 64 : 128);
+  constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
+  int e, mi, ni;
+  if (!weight_tile(wa, e, mi, ni)) return;
+  const int m0 = mi * 256, n0 = ni * (DUAL ? 128 : 256);
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
   MNLoader<T> la;
-  {
-    const int sc = m0 + MNLoader<T>::nb() * VEC;
-    la.col = sc < d ? reinterpret_cast<const char*>(x + sc) : nullptr;
-    la.ld = (int64_t)d * ES;
-    la.ridx = eti + o0;
-    la.rbase = 0;
-    la.klen = n_e;
-  }
+  la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
   MNLoader<T> lb;
   {
-    const int lc = MNLoader<T>::nb() * VEC;
+    // Logical column lc = pos0() of this thread -> (matrix, source column);
+    // setup() adds pos0() to first_pos, so pass n0 + source column - lc.
+    const int lc = MNLoader<T>::pos0();
     const int src = DUAL ? dual_src(lc) : 0;
-    const int sc = n0 + (DUAL ? dual_col(lc) : lc);
-    const T* S = src == 0 ? dA : dB;
-    lb.col = sc < h ? reinterpret_cast<const char*>(S + sc) : nullptr;
-    lb.ld = (int64_t)h * ES;
-    lb.ridx = nullptr;
-    lb.rbase = o0;
-    lb.klen = n_e;
+    const int sc = DUAL ? dual_col(lc) : lc;
+    lb.setup(reinterpret_cast<const char*>(src == 0 ? dA : dB), n0 + sc - lc, h,
+             (int64_t)h * ES, nullptr, o0, n_e);
   }
   Acc acc;
   gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
@@ -721,7 +854,7 @@ __global__ __launch_bounds__(NT) void b2_dw13(WeightArgs wa, const T* __restrict
   T* o1 = dW1 + (int64_t)e * d * h;
   T* o3 = DUAL ? dW3 + (int64_t)e * d * h : nullptr;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = m0 + acc_row(mt, i);
@@ -734,7 +867,7 @@ __global__ __launch_bounds__(NT) void b2_dw13(WeightArgs wa, const T* __restrict
         }
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NTL; ++nt) {
           const int c = n0 + acc_col(nt);
           if (c < h) Elem<T>::store(o1 + (int64_t)m * h + c, acc.c[mt][nt][i]);
         }
@@ -745,59 +878,44 @@ __global__ __launch_bounds__(NT) void b2_dw13(WeightArgs wa, const T* __restrict
 // B3 (slot pass k): dX = [dA | dB] [W1_e | W3_e]^T for the pass's rows,
 // dx[t] (+)= dX.  One GEMM over the concatenated 2h.
 template <typename T, bool DUAL>
-__global__ __launch_bounds__(NT) void b3_dx(RouteArgs ra, const T* __restrict__ dA,
-                                            const T* __restrict__ dB, const T* __restrict__ W1,
-                                            const T* __restrict__ W3,
-                                            const int32_t* __restrict__ list,
-                                            const int32_t* __restrict__ eti, int d, int h,
-                                            int mode, T* __restrict__ dx,
-                                            float* __restrict__ dxacc) {
+__global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict__ dA,
+                                               const T* __restrict__ dB,
+                                               const T* __restrict__ W1,
+                                               const T* __restrict__ W3,
+                                               const int32_t* __restrict__ list,
+                                               const int32_t* __restrict__ eti, int d, int h,
+                                               int mode, T* __restrict__ dx,
+                                               float* __restrict__ dxacc) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ int64_t s_t[TBM];
+  __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mtile = lid / ra.nN;
-  const int ntile = (int)(lid % ra.nN);
-  if (mtile >= ra.ntiles) return;
-  const int4 ds = ra.tiles[mtile];
-  if (ds.x < 0) return;
+  int4 ds;
+  int ntile;
+  if (!route_tile(ra, ds, ntile)) return;
   const int e = ds.x, rb = ds.y, re = ds.z;
-  const int n0 = ntile * 128;
+  const int n0 = ntile * 256;
   const int klen = DUAL ? 2 * h : h;
+  if (threadIdx.x < TBM) {
+    const int li = rb + threadIdx.x;
+    s_t[threadIdx.x] = li < re ? (int64_t)eti[list[li]] : -1;
+    s_g[threadIdx.x] = 1.0f;
+  }
 
   KLoader<T> la;
+  kloader_rows<T>(la, dA, list, nullptr, rb, re, h);
+  la.delta = DUAL ? (reinterpret_cast<const char*>(dB) - reinterpret_cast<const char*>(dA)) : 0;
+  la.ksplit = h;
+  la.klen = klen;
   KLoader<T> lb;
-  {
-    const int r = threadIdx.x >> 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int li = rb + r + 32 * i;
-      const int64_t p = li < re ? (int64_t)list[li] : -1;
-      la.p0[i] = p >= 0 ? reinterpret_cast<const char*>(dA + p * h) : nullptr;
-      la.p1[i] = (p >= 0 && DUAL) ? reinterpret_cast<const char*>(dB + p * h) : la.p0[i];
-      const int n = n0 + r + 32 * i;
-      lb.p0[i] = n < d ? reinterpret_cast<const char*>(W1 + ((int64_t)e * d + n) * h) : nullptr;
-      lb.p1[i] = (n < d && DUAL) ? reinterpret_cast<const char*>(W3 + ((int64_t)e * d + n) * h) : lb.p0[i];
-    }
-    la.ksplit = lb.ksplit = h;
-    la.klen = lb.klen = klen;
-  }
+  kloader_rows<T>(lb, W1 + (int64_t)e * d * h, nullptr, nullptr, n0, d, h);
+  lb.delta = DUAL ? (reinterpret_cast<const char*>(W3) - reinterpret_cast<const char*>(W1)) : 0;
+  lb.ksplit = h;
+  lb.klen = klen;
   Acc acc;
   gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, smem, acc);
-
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int li = rb + acc_row(mt, i);
-      if (li >= re) continue;
-      const int64_t t = eti[list[li]];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int c = n0 + acc_col(nt);
-        if (c < d) combine_store<T>(dx, dxacc, t * d + c, acc.c[mt][nt][i], mode);
-      }
-    }
-  }
+  __syncthreads();
+  combine_epilogue<T>(acc, s_t, s_g, n0, d, mode, dx, dxacc);
 }
 
 // ------------------------------------------------------------------ host
@@ -813,6 +931,7 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   p.pass_tiles = cdiv(dm.L, TBM) + dm.E;
   p.list_chunks = cdiv(p.R, LCH);
   const bool need_acc = dm.dtype == 1 && dm.K > 1;
+  const size_t wbytes = (size_t)dm.E * dm.d * dm.h * es;
   size_t o = 0;
   p.off_g = o;      o = align_up(o + (size_t)p.R * dm.h * es, 256);
   p.off_acc = o;    o = align_up(o + (need_acc ? (size_t)dm.L * dm.d * 4 : 0), 256);
@@ -824,6 +943,8 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   p.off_gatep = o;  o = align_up(o + (backward ? (size_t)p.R * 4 : 0), 256);
   p.off_tiles_route = o; o = align_up(o + (size_t)p.route_tiles * 16, 256);
   p.off_tiles_pass = o;  o = align_up(o + (size_t)dm.K * p.pass_tiles * 16, 256);
+  const int nW = backward ? 0 : (dm.act == 1 ? 3 : 2);   // W1T, W2T, (W3T)
+  p.off_wt = o;     o = align_up(o + nW * wbytes, 256);
   p.bytes = o;
   return p;
 }
@@ -879,30 +1000,46 @@ static int pass_mode(int K, int k, bool f32) {
 }
 
 template <typename T>
+static void transpose_w(const T* W, T* WT, int E, int R, int C, hipStream_t s) {
+  hipLaunchKernelGGL((transpose_weights<T>), dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64), E),
+                     dim3(256), 0, s, W, WT, R, C);
+}
+
+template <typename T>
 static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T* W1, const T* W3,
                       const T* W2, const int32_t* eti, const int32_t* offsets, const int32_t* tim,
                       const float* gates, T* y, T* A, T* B, char* ws, hipStream_t s) {
   const bool f32 = sizeof(T) == 4;
   const bool dual = dm.act == 1;
+  const size_t wel = (size_t)dm.E * dm.d * dm.h;
+  T* W1T = reinterpret_cast<T*>(ws + pl.off_wt);
+  T* W2T = W1T + wel;
+  T* W3T = dual ? W2T + wel : W1T;
+  {
+    LaunchTimer lt("weight_transpose", s);
+    transpose_w<T>(W1, W1T, dm.E, dm.d, dm.h, s);
+    if (dual) transpose_w<T>(W3, W3T, dm.E, dm.d, dm.h, s);
+    transpose_w<T>(W2, W2T, dm.E, dm.h, dm.d, s);
+  }
   Lists ls = build_lists(pl, dm, offsets, tim, gates, nullptr, ws, s);
   T* G = reinterpret_cast<T*>(ws + pl.off_g);
   float* acc = f32 ? reinterpret_cast<float*>(y) : reinterpret_cast<float*>(ws + pl.off_acc);
   {
     LaunchTimer lt("ffn_f1_gather_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 64 : 128)};
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256)};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
-      hipLaunchKernelGGL((f1_gather_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, x, W1, W3, eti,
-                         dm.d, dm.h, A, B, G);
+      hipLaunchKernelGGL((f1_gather_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
+                         eti, dm.d, dm.h, A, B, G);
     else
-      hipLaunchKernelGGL((f1_gather_glu<T, false>), dim3(grid), dim3(NT), 0, s, ra, x, W1, W3,
+      hipLaunchKernelGGL((f1_gather_glu<T, false>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
                          eti, dm.d, dm.h, A, B, G);
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_f2_down_combine", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 128)};
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256)};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
-    hipLaunchKernelGGL((f2_down_combine<T>), dim3(grid), dim3(NT), 0, s, ra, G, W2, ls.list, eti,
+    hipLaunchKernelGGL((f2_down_combine<T>), dim3(grid), dim3(NT), 0, s, ra, G, W2T, ls.list, eti,
                        gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc);
   }
 }
@@ -920,7 +1057,7 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   float* acc = f32 ? reinterpret_cast<float*>(dx) : reinterpret_cast<float*>(ws + pl.off_acc);
   {
     LaunchTimer lt("ffn_b1_dgrad_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, 128)};
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, 256)};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
       hipLaunchKernelGGL((b1_dgrad_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti,
@@ -931,14 +1068,14 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   {
     LaunchTimer lt("ffn_b0_dw2", s);
-    WeightArgs wa{dm.E, (int)cdiv(dm.h, 128), (int)cdiv(dm.d, 128)};
+    WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256)};
     const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
     hipLaunchKernelGGL((b0_dw2<T>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, dy, eti,
                        offsets, dm.d, dm.h, dW2);
   }
   {
     LaunchTimer lt("ffn_b2_dw13", s);
-    WeightArgs wa{dm.E, (int)cdiv(dm.d, 128), (int)cdiv(dm.h, dual ? 64 : 128)};
+    WeightArgs wa{dm.E, (int)cdiv(dm.d, 256), (int)cdiv(dm.h, dual ? 128 : 256)};
     const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
     if (dual)
       hipLaunchKernelGGL((b2_dw13<T, true>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, x, A,
@@ -949,7 +1086,7 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_b3_dx", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 128)};
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256)};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
       hipLaunchKernelGGL((b3_dx<T, true>), dim3(grid), dim3(NT), 0, s, ra, A, B, W1, W3, ls.list,
