@@ -41,6 +41,10 @@ EDGE = [
     (3000, 1, 1, "normal"),         # E = 1
     (777, 8, 8, "normal"),          # K = E
     (500, 5, 3, "normal"),          # E not a multiple of 4 (scalar loads)
+    (1000, 12, 3, "normal"),        # per-token register path, E below its vector width
+    (999, 36, 5, "normal"),         # per-token register path, 64-wide, E = 36
+    (513, 20, 20, "ties"),          # K = E on the per-token path, with ties
+    (2000, 64, 6, "misaligned"),    # E = 64 with logits not 16-byte aligned
     (999, 100, 7, "normal"),        # 512-token tiles
     (700, 256, 8, "normal"),        # largest E, 256-token tiles
     (300, 256, 255, "normal"),      # largest K

@@ -165,6 +165,83 @@ __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ lo
   }
 }
 
+// Step 1 for E <= 64: one thread per token with the token's logits in
+// registers (EV = E rounded up to a multiple of 4).  Top-K is K register
+// passes of an arg-max with ties to the lower id; no cross-lane traffic.
+template <int EV>
+__global__ __launch_bounds__(256) void k1_route_map_rows(const float* __restrict__ logits,
+                                                         int64_t L, int E, int K, int T, int C,
+                                                         int64_t Lpad, int32_t* __restrict__ tei,
+                                                         float* __restrict__ gates,
+                                                         uint8_t* __restrict__ map,
+                                                         int32_t* __restrict__ tilecnt) {
+  extern __shared__ uint4 smap_v[];
+  uint8_t* smap = reinterpret_cast<uint8_t*>(smap_v);
+  const int tile = blockIdx.x;
+  const int64_t t0 = (int64_t)tile * T;
+  const int nvec = (E * T) >> 4;
+  for (int i = threadIdx.x; i < nvec; i += 256) smap_v[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  for (int tl = threadIdx.x; tl < T; tl += 256) {
+    const int64_t t = t0 + tl;
+    if (t >= L) break;
+    float v[EV];
+    const float4* row = reinterpret_cast<const float4*>(logits + t * E);
+#pragma unroll
+    for (int j = 0; j < EV / 4; ++j) {
+      // E is a multiple of 4 here; vectors past the row are not read.
+      float4 q = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (4 * j < E) q = row[j];
+      v[4 * j] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
+    }
+    uint64_t sel = 0;
+    float vmax = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float bv = -INFINITY;
+      int be = -1;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) {
+        const bool cand = e < E && !((sel >> e) & 1ull);
+        if (cand && (be < 0 || v[e] > bv)) {
+          bv = v[e];
+          be = e;
+        }
+      }
+      if (k == 0) vmax = bv;
+      sel |= 1ull << be;
+    }
+    float ssum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e)
+      if ((sel >> e) & 1ull) ssum += expf(v[e] - vmax);
+    int slot = 0;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      if ((sel >> e) & 1ull) {
+        tei[t * K + slot] = e;
+        gates[t * K + slot] = expf(v[e] - vmax) / ssum;
+        smap[e * T + tl] = (uint8_t)(slot + 1);
+        ++slot;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nv = T >> 4;
+  for (int e = wave; e < E; e += 4) {
+    int cnt = 0;
+    for (int i = lane; i < nv; i += 64) {
+      const uint4 q = smap_v[(e * T >> 4) + i];
+      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = q;
+      cnt += nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) tilecnt[(int64_t)e * C + tile] = cnt;
+  }
+}
+
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
 // row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
 // the row sum when total is not null.
@@ -300,7 +377,18 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
   {
     LaunchTimer lt("dispatch_route_map", s);
     const int q = (E + 3) / 4;  // lanes needed per token
-    if (q <= 1) launch_k1<1>(pl, L, E, K, logits, tei, gates, map, cnt, s);
+    const bool rows_ok = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+    if (rows_ok && E <= 64) {
+      const size_t sh = (size_t)E * pl.T;
+#define MOE_K1R(EVV)                                                                            \
+  hipLaunchKernelGGL((k1_route_map_rows<EVV>), dim3(pl.C), dim3(256), sh, s, logits, L, E, K,   \
+                     pl.T, pl.C, pl.Lpad, tei, gates, map, cnt)
+      if (E <= 8) MOE_K1R(8);
+      else if (E <= 16) MOE_K1R(16);
+      else if (E <= 32) MOE_K1R(32);
+      else MOE_K1R(64);
+#undef MOE_K1R
+    } else if (q <= 1) launch_k1<1>(pl, L, E, K, logits, tei, gates, map, cnt, s);
     else if (q <= 2) launch_k1<2>(pl, L, E, K, logits, tei, gates, map, cnt, s);
     else if (q <= 4) launch_k1<4>(pl, L, E, K, logits, tei, gates, map, cnt, s);
     else if (q <= 8) launch_k1<8>(pl, L, E, K, logits, tei, gates, map, cnt, s);

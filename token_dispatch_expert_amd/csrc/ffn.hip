@@ -43,6 +43,8 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int NT = 512;                  // threads per workgroup
@@ -252,6 +254,92 @@ __device__ __forceinline__ void MNLoader<float>::store(char* lds) const {
   }
 }
 
+// bf16 operand tile kept as it lies in memory: 64 k-rows x 256 positions
+// (512 bytes per k-row).  MFMA fragments are read with the transposing LDS
+// read (ds_read_b64_tr_b16), so no register transpose is needed.  Thread t
+// copies 16-byte chunk (t & 31) of k-rows (t >> 5) + 16 i, i < 4.  The 32
+// chunks of a k-row are XOR-swizzled by 4 * (k & 3), so that the four k-rows
+// read together by a 16-lane group of the transposing read fall on
+// different banks.
+__device__ __forceinline__ int tlds_off(int k, int chunk) {
+  return k * 512 + ((chunk ^ ((k & 3) << 2)) << 4);
+}
+
+struct TLoader {
+  const char* col;        // byte address of position 0 of row 0 for this thread's chunk
+  bool colok;
+  int64_t ld;
+  const int32_t* ridx;
+  int64_t rbase;
+  int klen;
+  int64_t rnext[4];
+  uint4 reg[4];
+
+  __device__ static __forceinline__ int krow0() { return threadIdx.x >> 5; }
+
+  __device__ __forceinline__ void setup(const char* base, int first_pos, int limit, int64_t ld_,
+                                        const int32_t* ridx_, int64_t rbase_, int klen_) {
+    const int p = first_pos + (threadIdx.x & 31) * 8;
+    colok = p < limit;
+    col = base + (int64_t)(colok ? p : 0) * 2;
+    ld = ld_;
+    ridx = ridx_;
+    rbase = rbase_;
+    klen = klen_;
+    rows_of(0, rnext);
+  }
+  __device__ __forceinline__ void rows_of(int kt, int64_t (&rr)[4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = kt * 64 + krow0() + 16 * i;
+      const int kk = (colok && k < klen) ? k : 0;
+      rr[i] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
+    }
+  }
+  __device__ __forceinline__ void fetch(int kt) {
+    int64_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = rnext[i];
+    rows_of(kt + 1, rnext);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = colok && kt * 64 + krow0() + 16 * i < klen;
+      reg[i] = sel16(ok, *reinterpret_cast<const uint4*>(col + r[i] * ld));
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int c = threadIdx.x & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(lds + tlds_off(krow0() + 16 * i, c)) = reg[i];
+  }
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Fragment of 32 positions p0 .. p0+31 and k = kbase .. kbase+15 from a
+// TLoader tile: lane l gets position p0 + (l & 31) and the 8 k values
+// kbase + 8 (l >> 5) + 0..7, from two transposing reads of 4 k-rows each.
+// (Within a 16-lane group the read hands lane i element i & 3 of the
+// 8-byte chunk addressed by lane 4 m + (i >> 2), for m = 0..3.)
+__device__ __forceinline__ uint4 tr_fragment(const char* tile, int p0, int kbase) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i = lane & 15;
+  const int pos = p0 + 16 * (g & 1) + 4 * (i & 3);
+  const int k0 = kbase + 8 * (g >> 1) + (i >> 2);
+  const int cb = ((pos >> 3) & 31), half = (pos & 7) * 2;
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  const lds_v4* a0 = reinterpret_cast<const lds_v4*>(
+      (__attribute__((address_space(3))) const char*)(tile + tlds_off(k0, cb) + half));
+  const lds_v4* a1 = reinterpret_cast<const lds_v4*>(
+      (__attribute__((address_space(3))) const char*)(tile + tlds_off(k0 + 4, cb) + half));
+  const v4i16_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4*>(a0));
+  const v4i16_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4*>(a1));
+  const uint2 u0 = __builtin_bit_cast(uint2, x0);
+  const uint2 u1 = __builtin_bit_cast(uint2, x1);
+  return make_uint4(u0.x, u0.y, u1.x, u1.y);
+}
+
 // ------------------------------------------------------------------ MFMA
 
 template <typename T>
@@ -303,8 +391,26 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
   }
 }
 
-// Main loop over nk k-tiles; result in acc (zero when nk == 0).
-template <typename T, class LA, class LB>
+// One k-tile of MFMAs on two TLoader tiles (bf16).
+__device__ __forceinline__ void mma_ktile_tr(const char* As, const char* Bs, Acc& acc) {
+  const int wm = wave_m(), wn = wave_n();
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    uint4 a[MT], b[NTL];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = tr_fragment(As, wm * 128 + mt * 32, kc * 16);
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) b[nt] = tr_fragment(Bs, wn * 64 + nt * 32, kc * 16);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<bf16_t>(a[mt], b[nt], acc.c[mt][nt]);
+  }
+}
+
+// Main loop over nk k-tiles; result in acc (zero when nk == 0).  TR: both
+// operands are TLoader tiles read with the transposing LDS read.
+template <typename T, class LA, class LB, bool TR = false>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -326,7 +432,8 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
       la.fetch(kt + 1);
       lb.fetch(kt + 1);
     }
-    mma_ktile<T>(cur, cur + OPB, acc);
+    if constexpr (TR) mma_ktile_tr(cur, cur + OPB, acc);
+    else mma_ktile<T>(cur, cur + OPB, acc);
     if (more) {
       la.store(nxt);
       lb.store(nxt + OPB);
@@ -797,12 +904,13 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
   const int m0 = mi * 256, n0 = ni * 256;
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
-  MNLoader<T> la;
+  using LD = typename std::conditional<std::is_same<T, bf16_t>::value, TLoader, MNLoader<T>>::type;
+  LD la;
   la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
-  MNLoader<T> lb;
+  LD lb;
   lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
   Acc acc;
-  gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T, LD, LD, std::is_same<T, bf16_t>::value>(la, lb, (n_e + KT - 1) / KT, smem, acc);
 
   T* out = dW2 + (int64_t)e * h * d;
 #pragma unroll
@@ -836,20 +944,24 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
   const int m0 = mi * 256, n0 = ni * (DUAL ? 128 : 256);
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
-  MNLoader<T> la;
+  constexpr bool TR = std::is_same<T, bf16_t>::value;
+  using LD = typename std::conditional<TR, TLoader, MNLoader<T>>::type;
+  LD la;
   la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-  MNLoader<T> lb;
+  LD lb;
   {
-    // Logical column lc = pos0() of this thread -> (matrix, source column);
-    // setup() adds pos0() to first_pos, so pass n0 + source column - lc.
-    const int lc = MNLoader<T>::pos0();
+    // Logical column lc of this thread's first position -> (matrix, source
+    // column); setup() adds lc to first_pos, so pass n0 + source column - lc.
+    int lc;
+    if constexpr (TR) lc = (threadIdx.x & 31) * 8;
+    else lc = MNLoader<T>::pos0();
     const int src = DUAL ? dual_src(lc) : 0;
     const int sc = DUAL ? dual_col(lc) : lc;
     lb.setup(reinterpret_cast<const char*>(src == 0 ? dA : dB), n0 + sc - lc, h,
              (int64_t)h * ES, nullptr, o0, n_e);
   }
   Acc acc;
-  gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T, LD, LD, TR>(la, lb, (n_e + KT - 1) / KT, smem, acc);
 
   T* o1 = dW1 + (int64_t)e * d * h;
   T* o3 = DUAL ? dW3 + (int64_t)e * d * h : nullptr;
