@@ -68,6 +68,63 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+ROCPROF_NAMES = {   # library timer name -> kernel symbol base name in rocprofv3 output
+    "ffn_f1_gather_glu": "f1_gather_glu",
+    "ffn_f2_down_combine": "f2_down_combine",
+    "ffn_b1_dgrad_glu": "b1_dgrad_glu",
+    "ffn_b0_dw2": "b0_dw2",
+    "ffn_b2_dw13": "b2_dw13",
+    "ffn_b3_dx": "b3_dx",
+    "dispatch_route_map": "k1_route_map",
+    "dispatch_scatter": "k3_scatter",
+}
+
+
+def _counter_means(csv_path, counter):
+    import csv
+    import re
+    sums, counts = {}, {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
+            name = re.sub(r"<.*", "", name).split("::")[-1]
+            sums[name] = sums.get(name, 0.0) + float(r["Counter_Value"])
+            counts[name] = counts.get(name, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def record_traffic(dirs, workload):
+    """Write profiles/traffic.json from four rocprofv3 --pmc runs (csv output
+    directories): FETCH_SIZE and WRITE_SIZE of bench.py, and the same two
+    counters of `bench.py --copy-calibration 1024` (a plain copy of known
+    size, used to scale the counters to bytes)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    csvf = lambda d: os.path.join(d, "run_counter_collection.csv")  # noqa: E731
+    copy_bytes = 1024 << 20
+    cf = max(_counter_means(csvf(cfetch_dir), "FETCH_SIZE").values())
+    cw = max(_counter_means(csvf(cwrite_dir), "WRITE_SIZE").values())
+    fscale, wscale = copy_bytes / cf, copy_bytes / cw
+    fetch = _counter_means(csvf(fetch_dir), "FETCH_SIZE")
+    write = _counter_means(csvf(write_dir), "WRITE_SIZE")
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(p)) if os.path.exists(p) else {}
+    ent = {}
+    for timer, sym in ROCPROF_NAMES.items():
+        if sym in fetch and sym in write:
+            ent[timer] = {"source_hash": source_hash(),
+                          "fetch_bytes_per_launch": fetch[sym] * fscale,
+                          "write_bytes_per_launch": write[sym] * wscale,
+                          "bytes_per_launch": fetch[sym] * fscale + write[sym] * wscale}
+    rec[workload] = ent
+    rec["_scale"] = {"fetch_size_bytes_per_unit": fscale, "write_size_bytes_per_unit": wscale,
+                     "reference": "plain device copy of 1 GiB"}
+    with open(p, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(ent, indent=1))
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources; else None."""
@@ -128,7 +185,27 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (scale reference "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc csv output directories "
+                         "and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.record_traffic, W.CONFIGS[args.config].name)
+        return
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

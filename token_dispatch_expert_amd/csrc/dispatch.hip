@@ -340,9 +340,11 @@ void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, in
 DispatchPlan plan_dispatch(int64_t L, int E, int K) {
   (void)K;
   DispatchPlan p;
-  int T = (32768 / E) / 256 * 256;
-  if (T > 1024) T = 1024;
-  if (T < 256) T = 256;
+  // T is a power of two in [256, 1024] (the scatter kernel splits a
+  // wavefront into T/16-lane row segments), with E * T <= 32 KB of LDS
+  // where possible (E * T <= 64 KB always, since E <= 256).
+  int T = 1024;
+  while (T > 256 && E * T > 32768) T >>= 1;
   p.T = T;
   p.C = (int)((L + T - 1) / T);
   p.Lpad = (int64_t)p.C * T;

@@ -89,6 +89,7 @@ __device__ __forceinline__ uint4 sel16(bool ok, uint4 v) {
 // Rows that are out of range point at a valid row and are zeroed.
 template <typename T>
 struct KLoader {
+  static constexpr bool kDirect = false;
   const char* p0[4];
   uint32_t valid;
   int64_t delta;
@@ -110,6 +111,73 @@ struct KLoader {
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + lds_off(r + 64 * i, c)) = reg[i];
   }
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane straight from global memory into LDS: lane i of the
+// wavefront lands at lds_base + 16 i (lds_base is wavefront-uniform).
+__device__ __forceinline__ void load_to_lds(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// Direct-to-LDS version of KLoader (same tile and swizzle).  Wavefront w
+// fills rows w*32 .. w*32+31 with four 1 KB loads; in load j lane l writes
+// LDS row w*32 + 8 j + (l >> 3), physical chunk l & 7, so it fetches the
+// logical chunk (l & 7) ^ swizzle(row) of that row.  Absent rows and k
+// beyond klen read the zero page instead.
+template <typename T>
+struct KLoaderD {
+  static constexpr bool kDirect = true;
+  const char* rp[4];      // row start (absent row: nullptr)
+  int cj[4];              // logical chunk fetched in load j
+  const char* zero;       // 16 zero bytes
+  int64_t delta;
+  int ksplit, klen;
+
+  __device__ static __forceinline__ int row_of(int j) {
+    return (threadIdx.x >> 6) * 32 + 8 * j + ((threadIdx.x & 63) >> 3);
+  }
+  __device__ __forceinline__ void init_chunks() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = row_of(j);
+      cj[j] = (threadIdx.x & 7) ^ ((r ^ (r >> 3)) & 7);
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* lds) const {
+    constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = kt * KT + cj[j] * VEC;
+      const bool ok = rp[j] != nullptr && k < klen;
+      const char* g = k < ksplit ? rp[j] + (int64_t)k * ES : rp[j] + delta + (int64_t)(k - ksplit) * ES;
+      load_to_lds(ok ? g : zero, lds + (w * 32 + 8 * j) * ROWB);
+    }
+  }
+};
+
+// Row pointers of a KLoaderD: LDS row r of the tile is list entry rb + r
+// (identity list when list == nullptr), optionally mapped through `gather`;
+// row index idx lives at base + idx * row_elems.
+template <typename T>
+__device__ __forceinline__ void kloaderd_rows(KLoaderD<T>& la, const T* base, const int32_t* list,
+                                              const int32_t* gather, int rb, int re,
+                                              int64_t row_elems, const char* zero) {
+  la.zero = zero;
+  la.init_chunks();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int li = rb + KLoaderD<T>::row_of(j);
+    const char* p = nullptr;
+    if (li < re) {
+      int64_t idx = list != nullptr ? (int64_t)list[li] : (int64_t)li;
+      if (gather != nullptr) idx = gather[idx];
+      p = reinterpret_cast<const char*>(base + idx * row_elems);
+    }
+    la.rp[j] = p;
+  }
+}
 
 // Row pointers of a KLoader: LDS row j of the tile is list entry rb + j
 // (the identity list when list == nullptr), optionally mapped through
@@ -147,6 +215,7 @@ __device__ __forceinline__ void kloader_rows(KLoader<T>& la, const T* base, cons
 // consecutive lanes cover both row parities of an LDS cycle.
 template <typename T>
 struct MNLoader {
+  static constexpr bool kDirect = false;
   const char* col;
   bool colok;
   int64_t ld;
@@ -266,6 +335,7 @@ __device__ __forceinline__ int tlds_off(int k, int chunk) {
 }
 
 struct TLoader {
+  static constexpr bool kDirect = false;
   const char* col;        // byte address of position 0 of row 0 for this thread's chunk
   bool colok;
   int64_t ld;
@@ -312,6 +382,56 @@ struct TLoader {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(lds + tlds_off(krow0() + 16 * i, c)) = reg[i];
+  }
+};
+
+// Direct-to-LDS version of TLoader (same tile and swizzle).  Wavefront w
+// fills k-rows w*8 .. w*8+7 with four 1 KB loads; in load j lane l writes
+// k-row w*8 + 2 j + (l >> 5), physical chunk l & 31, so it fetches logical
+// chunk (l & 31) ^ (4 (k & 3)) = positions 8 c .. 8 c + 7.
+struct TLoaderD {
+  static constexpr bool kDirect = true;
+  const char* col[4];     // position column of load j (row 0); absent: nullptr
+  int64_t ld;
+  const int32_t* ridx;
+  int64_t rbase;
+  int klen;
+  const char* zero;
+  int64_t rnext[4];
+
+  __device__ static __forceinline__ int krow(int j) {
+    return (threadIdx.x >> 6) * 8 + 2 * j + ((threadIdx.x & 63) >> 5);
+  }
+  __device__ static __forceinline__ int lpos(int j) {   // logical position of load j
+    return (((threadIdx.x & 31) ^ ((krow(j) & 3) << 2))) * 8;
+  }
+  // Positions of the tile come from b0 (and, for dual tiles, b1 by the
+  // interleave of dual_src / dual_col) starting at first_pos; `limit`
+  // positions per row, ld bytes between rows.
+  template <bool DUALCOL>
+  __device__ __forceinline__ void setup(const char* b0, const char* b1, int first_pos, int limit,
+                                        int64_t ld_, const int32_t* ridx_, int64_t rbase_,
+                                        int klen_, const char* zero_);
+  __device__ __forceinline__ void rows_of(int kt, int64_t (&rr)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = kt * 64 + krow(j);
+      const int kk = k < klen ? k : 0;
+      rr[j] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* lds) {
+    int64_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = rnext[j];
+    rows_of(kt + 1, rnext);
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = col[j] != nullptr && kt * 64 + krow(j) < klen;
+      const char* g = col[j] + r[j] * ld;
+      load_to_lds(ok ? g : zero, lds + (w * 8 + 2 * j) * 512);
+    }
   }
 };
 
@@ -419,25 +539,26 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc.c[mt][nt][i] = 0.f;
   if (nk <= 0) return;
-  la.fetch(0);
-  lb.fetch(0);
-  la.store(smem);
-  lb.store(smem + OPB);
+  constexpr bool DA = LA::kDirect, DB = LB::kDirect;
+  if constexpr (DA) la.issue(0, smem); else { la.fetch(0); la.store(smem); }
+  if constexpr (DB) lb.issue(0, smem + OPB); else { lb.fetch(0); lb.store(smem + OPB); }
+  if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = smem + (kt & 1) * STAGE;
     char* nxt = smem + ((kt + 1) & 1) * STAGE;
     const bool more = kt + 1 < nk;
     if (more) {
-      la.fetch(kt + 1);
-      lb.fetch(kt + 1);
+      if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
+      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
     }
     if constexpr (TR) mma_ktile_tr(cur, cur + OPB, acc);
     else mma_ktile<T>(cur, cur + OPB, acc);
     if (more) {
-      la.store(nxt);
-      lb.store(nxt + OPB);
+      if constexpr (!DA) la.store(nxt);
+      if constexpr (!DB) lb.store(nxt + OPB);
     }
+    if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 }
@@ -458,6 +579,25 @@ __device__ __forceinline__ int acc_col(int nt) {
 // 1 holds matrix 1 at the same source column.
 __device__ __forceinline__ int dual_src(int lc) { return (lc >> 5) & 1; }
 __device__ __forceinline__ int dual_col(int lc) { return (lc >> 6) * 32 + (lc & 31); }
+
+template <bool DUALCOL>
+__device__ __forceinline__ void TLoaderD::setup(const char* b0, const char* b1, int first_pos,
+                                                int limit, int64_t ld_, const int32_t* ridx_,
+                                                int64_t rbase_, int klen_, const char* zero_) {
+  ld = ld_;
+  ridx = ridx_;
+  rbase = rbase_;
+  klen = klen_;
+  zero = zero_;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int lc = lpos(j);
+    const int src = DUALCOL ? dual_src(lc) : 0;
+    const int p = first_pos + (DUALCOL ? dual_col(lc) : lc);
+    col[j] = p < limit ? (src == 0 ? b0 : b1) + (int64_t)p * 2 : nullptr;
+  }
+  rows_of(0, rnext);
+}
 
 template <typename T>
 __device__ __forceinline__ float silu_of(float a);
@@ -500,9 +640,12 @@ __global__ __launch_bounds__(256) void transpose_weights(const T* __restrict__ W
 // into row tiles of at most TBM rows.  desc[g][i] = {e, begin, end, 0} or
 // {-1, 0, 0, 0} past the last tile.
 __global__ __launch_bounds__(256) void tile_table(const int32_t* __restrict__ seg, int E,
-                                                  int64_t max_tiles, int4* __restrict__ desc) {
+                                                  int64_t max_tiles, int4* __restrict__ desc,
+                                                  uint4* __restrict__ zero_page) {
   __shared__ int s_start[257];
   __shared__ int scratch[4];
+  if (zero_page != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 16)
+    zero_page[threadIdx.x] = make_uint4(0, 0, 0, 0);
   const int grp = blockIdx.y;
   const int32_t* off = seg + (int64_t)grp * (E + 1);
   const int tid = threadIdx.x;
@@ -618,6 +761,7 @@ struct RouteArgs {            // row tiles over routes or slot-pass lists
   const int4* tiles;
   int64_t ntiles;             // upper bound, rows of the grid
   int nN;                     // column tiles
+  const char* zero;           // 16 zero bytes (workspace)
 };
 
 // Tile coordinates of a route-major GEMM workgroup; false if it has no work.
@@ -648,27 +792,23 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   const int e = ds.x, rb = ds.y, re = ds.z;
   const int n0 = ntile * (DUAL ? 128 : 256);
 
-  KLoader<T> la;
-  kloader_rows<T>(la, x, nullptr, eti, rb, re, d);
+  KLoaderD<T> la;
+  kloaderd_rows<T>(la, x, nullptr, eti, rb, re, d, ra.zero);
   la.delta = 0;
   la.ksplit = la.klen = d;
-  KLoader<T> lb;
-  {
-    const int r = threadIdx.x >> 3;
-    lb.valid = 0;
+  KLoaderD<T> lb;
+  lb.zero = ra.zero;
+  lb.init_chunks();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = r + 64 * i;
-      const int src = DUAL ? dual_src(lr) : 0;
-      const int sc = n0 + (DUAL ? dual_col(lr) : lr);
-      const bool ok = sc < h;
-      const T* Wm = (src == 0 ? W1T : W3T) + ((int64_t)e * h + (ok ? sc : 0)) * d;
-      lb.p0[i] = reinterpret_cast<const char*>(Wm);
-      lb.valid |= (ok ? 1u : 0u) << i;
-    }
-    lb.delta = 0;
-    lb.ksplit = lb.klen = d;
+  for (int j = 0; j < 4; ++j) {
+    const int lr = KLoaderD<T>::row_of(j);
+    const int src = DUAL ? dual_src(lr) : 0;
+    const int sc = n0 + (DUAL ? dual_col(lr) : lr);
+    lb.rp[j] = sc < h ? reinterpret_cast<const char*>((src == 0 ? W1T : W3T) + ((int64_t)e * h + sc) * d)
+                      : nullptr;
   }
+  lb.delta = 0;
+  lb.ksplit = lb.klen = d;
   Acc acc;
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
 
@@ -783,12 +923,12 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
     s_g[threadIdx.x] = g;
   }
 
-  KLoader<T> la;
-  kloader_rows<T>(la, Gb, list, nullptr, rb, re, h);
+  KLoaderD<T> la;
+  kloaderd_rows<T>(la, Gb, list, nullptr, rb, re, h, ra.zero);
   la.delta = 0;
   la.ksplit = la.klen = h;
-  KLoader<T> lb;
-  kloader_rows<T>(lb, W2T + (int64_t)e * d * h, nullptr, nullptr, n0, d, h);
+  KLoaderD<T> lb;
+  kloaderd_rows<T>(lb, W2T + (int64_t)e * d * h, nullptr, nullptr, n0, d, h, ra.zero);
   lb.delta = 0;
   lb.ksplit = lb.klen = h;
   Acc acc;
@@ -819,12 +959,12 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
     s_g[threadIdx.x] = p < re ? gate_p[p] : 0.f;
   }
 
-  KLoader<T> la;
-  kloader_rows<T>(la, dy, nullptr, eti, rb, re, d);
+  KLoaderD<T> la;
+  kloaderd_rows<T>(la, dy, nullptr, eti, rb, re, d, ra.zero);
   la.delta = 0;
   la.ksplit = la.klen = d;
-  KLoader<T> lb;
-  kloader_rows<T>(lb, W2 + (int64_t)e * h * d, nullptr, nullptr, n0, h, d);
+  KLoaderD<T> lb;
+  kloaderd_rows<T>(lb, W2 + (int64_t)e * h * d, nullptr, nullptr, n0, h, d, ra.zero);
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
   Acc acc;
@@ -877,6 +1017,7 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
 
 struct WeightArgs {           // weight-gradient tiles: E x nM x nN
   int E, nM, nN;
+  const char* zero;           // 16 zero bytes (workspace)
 };
 
 __device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& mi, int& ni) {
@@ -904,13 +1045,20 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
   const int m0 = mi * 256, n0 = ni * 256;
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
-  using LD = typename std::conditional<std::is_same<T, bf16_t>::value, TLoader, MNLoader<T>>::type;
-  LD la;
-  la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
-  LD lb;
-  lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
   Acc acc;
-  gemm_mainloop<T, LD, LD, std::is_same<T, bf16_t>::value>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    TLoaderD la, lb;
+    la.setup<false>(reinterpret_cast<const char*>(Gs), nullptr, m0, h, (int64_t)h * ES, nullptr,
+                    o0, n_e, wa.zero);
+    lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
+                    0, n_e, wa.zero);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  } else {
+    MNLoader<T> la, lb;
+    la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
+    lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  }
 
   T* out = dW2 + (int64_t)e * h * d;
 #pragma unroll
@@ -944,24 +1092,26 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
   const int m0 = mi * 256, n0 = ni * (DUAL ? 128 : 256);
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
 
-  constexpr bool TR = std::is_same<T, bf16_t>::value;
-  using LD = typename std::conditional<TR, TLoader, MNLoader<T>>::type;
-  LD la;
-  la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-  LD lb;
-  {
+  Acc acc;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    TLoaderD la, lb;
+    la.setup<false>(reinterpret_cast<const char*>(x), nullptr, m0, d, (int64_t)d * ES, eti + o0, 0,
+                    n_e, wa.zero);
+    lb.setup<DUAL>(reinterpret_cast<const char*>(dA), reinterpret_cast<const char*>(dB), n0, h,
+                   (int64_t)h * ES, nullptr, o0, n_e, wa.zero);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+  } else {
+    MNLoader<T> la, lb;
+    la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
     // Logical column lc of this thread's first position -> (matrix, source
     // column); setup() adds lc to first_pos, so pass n0 + source column - lc.
-    int lc;
-    if constexpr (TR) lc = (threadIdx.x & 31) * 8;
-    else lc = MNLoader<T>::pos0();
+    const int lc = MNLoader<T>::pos0();
     const int src = DUAL ? dual_src(lc) : 0;
     const int sc = DUAL ? dual_col(lc) : lc;
     lb.setup(reinterpret_cast<const char*>(src == 0 ? dA : dB), n0 + sc - lc, h,
              (int64_t)h * ES, nullptr, o0, n_e);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   }
-  Acc acc;
-  gemm_mainloop<T, LD, LD, TR>(la, lb, (n_e + KT - 1) / KT, smem, acc);
 
   T* o1 = dW1 + (int64_t)e * d * h;
   T* o3 = DUAL ? dW3 + (int64_t)e * d * h : nullptr;
@@ -1014,13 +1164,13 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
     s_g[threadIdx.x] = 1.0f;
   }
 
-  KLoader<T> la;
-  kloader_rows<T>(la, dA, list, nullptr, rb, re, h);
+  KLoaderD<T> la;
+  kloaderd_rows<T>(la, dA, list, nullptr, rb, re, h, ra.zero);
   la.delta = DUAL ? (reinterpret_cast<const char*>(dB) - reinterpret_cast<const char*>(dA)) : 0;
   la.ksplit = h;
   la.klen = klen;
-  KLoader<T> lb;
-  kloader_rows<T>(lb, W1 + (int64_t)e * d * h, nullptr, nullptr, n0, d, h);
+  KLoaderD<T> lb;
+  kloaderd_rows<T>(lb, W1 + (int64_t)e * d * h, nullptr, nullptr, n0, d, h, ra.zero);
   lb.delta = DUAL ? (reinterpret_cast<const char*>(W3) - reinterpret_cast<const char*>(W1)) : 0;
   lb.ksplit = h;
   lb.klen = klen;
@@ -1057,6 +1207,7 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   p.off_tiles_pass = o;  o = align_up(o + (size_t)dm.K * p.pass_tiles * 16, 256);
   const int nW = backward ? 0 : (dm.act == 1 ? 3 : 2);   // W1T, W2T, (W3T)
   p.off_wt = o;     o = align_up(o + nW * wbytes, 256);
+  p.off_zero = o;   o = align_up(o + 256, 256);
   p.bytes = o;
   return p;
 }
@@ -1066,6 +1217,7 @@ struct Lists {
   int32_t* pe_off;
   int4* tiles_route;
   int4* tiles_pass;
+  uint4* zero;
 };
 
 static Lists build_lists(const FfnPlan& pl, const FfnDims& dm, const int32_t* offsets,
@@ -1079,11 +1231,12 @@ static Lists build_lists(const FfnPlan& pl, const FfnDims& dm, const int32_t* of
   ls.pe_off = reinterpret_cast<int32_t*>(ws + pl.off_peoff);
   ls.tiles_route = reinterpret_cast<int4*>(ws + pl.off_tiles_route);
   ls.tiles_pass = reinterpret_cast<int4*>(ws + pl.off_tiles_pass);
+  ls.zero = reinterpret_cast<uint4*>(ws + pl.off_zero);
   const int C = (int)pl.list_chunks;
   {
     LaunchTimer lt("route_tiles", s);
     hipLaunchKernelGGL(tile_table, dim3((unsigned)cdiv(pl.route_tiles, 256), 1), dim3(256), 0, s,
-                       offsets, dm.E, pl.route_tiles, ls.tiles_route);
+                       offsets, dm.E, pl.route_tiles, ls.tiles_route, ls.zero);
   }
   {
     LaunchTimer lt("slot_lists", s);
@@ -1099,7 +1252,7 @@ static Lists build_lists(const FfnPlan& pl, const FfnDims& dm, const int32_t* of
   {
     LaunchTimer lt("pass_tiles", s);
     hipLaunchKernelGGL(tile_table, dim3((unsigned)cdiv(pl.pass_tiles, 256), dm.K), dim3(256), 0,
-                       s, ls.pe_off, dm.E, pl.pass_tiles, ls.tiles_pass);
+                       s, ls.pe_off, dm.E, pl.pass_tiles, ls.tiles_pass, (uint4*)nullptr);
   }
   return ls;
 }
@@ -1138,7 +1291,7 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
   float* acc = f32 ? reinterpret_cast<float*>(y) : reinterpret_cast<float*>(ws + pl.off_acc);
   {
     LaunchTimer lt("ffn_f1_gather_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256)};
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
       hipLaunchKernelGGL((f1_gather_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
@@ -1149,7 +1302,7 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_f2_down_combine", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256)};
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     hipLaunchKernelGGL((f2_down_combine<T>), dim3(grid), dim3(NT), 0, s, ra, G, W2T, ls.list, eti,
                        gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc);
@@ -1169,7 +1322,7 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   float* acc = f32 ? reinterpret_cast<float*>(dx) : reinterpret_cast<float*>(ws + pl.off_acc);
   {
     LaunchTimer lt("ffn_b1_dgrad_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, 256)};
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, 256), (const char*)ls.zero};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
       hipLaunchKernelGGL((b1_dgrad_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti,
@@ -1180,14 +1333,14 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   {
     LaunchTimer lt("ffn_b0_dw2", s);
-    WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256)};
+    WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256), (const char*)ls.zero};
     const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
     hipLaunchKernelGGL((b0_dw2<T>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, dy, eti,
                        offsets, dm.d, dm.h, dW2);
   }
   {
     LaunchTimer lt("ffn_b2_dw13", s);
-    WeightArgs wa{dm.E, (int)cdiv(dm.d, 256), (int)cdiv(dm.h, dual ? 128 : 256)};
+    WeightArgs wa{dm.E, (int)cdiv(dm.d, 256), (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero};
     const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
     if (dual)
       hipLaunchKernelGGL((b2_dw13<T, true>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, x, A,
@@ -1198,7 +1351,7 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_b3_dx", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256)};
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
     if (dual)
       hipLaunchKernelGGL((b3_dx<T, true>), dim3(grid), dim3(NT), 0, s, ra, A, B, W1, W3, ls.list,

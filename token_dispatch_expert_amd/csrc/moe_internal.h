@@ -46,7 +46,7 @@ struct FfnPlan {
   int64_t pass_tiles;    // upper bound of M tiles per slot pass
   int64_t list_chunks;   // chunks of the slot-list builder
   size_t off_g, off_acc, off_slot, off_list, off_cnt, off_base, off_peoff, off_gatep;
-  size_t off_tiles_route, off_tiles_pass, off_wt, bytes;
+  size_t off_tiles_route, off_tiles_pass, off_wt, off_zero, bytes;
 };
 FfnPlan plan_ffn(const FfnDims& dm, bool backward);
 
