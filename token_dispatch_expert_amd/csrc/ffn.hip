@@ -495,36 +495,57 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
   const int r = lane & 31, g = lane >> 5;
+  // Fragments of k-chunk kc + 1 are read while the MFMAs of kc issue.
+  uint4 a[2][MT], b[2][NTL];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    a[0][mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, g));
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt)
+    b[0][nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, g));
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    uint4 a[MT], b[NTL];
+    const int cb = kc & 1, nb = cb ^ 1;
+    if (kc < 3) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        a[nb][mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, (kc + 1) * 2 + g));
+#pragma unroll
+      for (int nt = 0; nt < NTL; ++nt)
+        b[nb][nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, (kc + 1) * 2 + g));
+    }
+    // keep the reads above ahead of this chunk's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      a[mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, kc * 2 + g));
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt)
-      b[nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, kc * 2 + g));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[mt], b[nt], acc.c[mt][nt]);
+      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[cb][mt], b[cb][nt], acc.c[mt][nt]);
   }
 }
 
 // One k-tile of MFMAs on two TLoader tiles (bf16).
 __device__ __forceinline__ void mma_ktile_tr(const char* As, const char* Bs, Acc& acc) {
   const int wm = wave_m(), wn = wave_n();
+  uint4 a[2][MT], b[2][NTL];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) a[0][mt] = tr_fragment(As, wm * 128 + mt * 32, 0);
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt) b[0][nt] = tr_fragment(Bs, wn * 64 + nt * 32, 0);
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    uint4 a[MT], b[NTL];
+    const int cb = kc & 1, nb = cb ^ 1;
+    if (kc < 3) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = tr_fragment(As, wm * 128 + mt * 32, kc * 16);
+      for (int mt = 0; mt < MT; ++mt) a[nb][mt] = tr_fragment(As, wm * 128 + mt * 32, (kc + 1) * 16);
 #pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) b[nt] = tr_fragment(Bs, wn * 64 + nt * 32, kc * 16);
+      for (int nt = 0; nt < NTL; ++nt) b[nb][nt] = tr_fragment(Bs, wn * 64 + nt * 32, (kc + 1) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<bf16_t>(a[mt], b[nt], acc.c[mt][nt]);
+      for (int nt = 0; nt < NTL; ++nt)
+        acc.c[mt][nt] = mfma_k8<bf16_t>(a[cb][mt], b[cb][nt], acc.c[mt][nt]);
   }
 }
 
