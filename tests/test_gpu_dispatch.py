@@ -52,6 +52,13 @@ EDGE = [
     (4096, 16, 2, "empty_mid"),     # expert 7 never chosen
     (4096, 8, 1, "all_one"),        # every token on expert 3
     (5000, 32, 4, "misaligned"),    # logits not 16-byte aligned
+    (1500, 16, 4, "ties"),          # streaming router, ties at the K-th value
+    (600, 8, 8, "ties"),            # streaming router, K = E with ties
+    (2000, 4, 1, "ties"),           # smallest streaming E, K = 1
+    (1024, 32, 3, "signed_zero"),   # -0.0 and +0.0 rank as equal
+    (2500, 28, 7, "normal"),        # streaming router, 7 chunks per row
+    (3000, 40, 8, "normal"),        # 64-bit expert mask with E < 64
+    (3001, 64, 8, "ties"),          # largest streaming E and K
 ]
 
 
@@ -63,6 +70,9 @@ def test_dispatch_edges(L, E, K, kind):
     z = torch.randn(L, E, generator=g)
     if kind == "ties":
         z = torch.randint(-2, 3, (L, E), generator=g).float()
+    elif kind == "signed_zero":
+        z = torch.randint(-1, 2, (L, E), generator=g).float() * 0.0
+        z[torch.rand(L, E, generator=g) < 0.05] = 1.0
     elif kind == "empty_mid":
         z[:, 7] = -1e4
     elif kind == "all_one":

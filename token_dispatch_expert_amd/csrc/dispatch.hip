@@ -242,6 +242,139 @@ __global__ __launch_bounds__(256) void k1_route_map_rows(const float* __restrict
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int EB> struct MaskT { using type = uint32_t; };
+template <> struct MaskT<64> { using type = uint64_t; };
+
+__device__ __forceinline__ int lowest_bit(uint32_t m) { return __builtin_ctz(m); }
+__device__ __forceinline__ int lowest_bit(uint64_t m) { return __builtin_ctzll(m); }
+__device__ __forceinline__ int bit_count(uint32_t m) { return __builtin_popcount(m); }
+__device__ __forceinline__ int bit_count(uint64_t m) { return __builtin_popcountll(m); }
+
+// Step 1, streaming form for E <= EB (E % 4 == 0, EB in {16, 32, 64}) and a
+// compile-time K <= 8: one tile of 256 tokens per workgroup, one token per
+// lane.  Each wavefront copies the 64 consecutive logit rows of its tokens
+// (one contiguous run of 256 E bytes) straight into LDS with 1 KB
+// global_load_lds transfers; each lane then reads its own row back, starting
+// at a lane-dependent 16-byte chunk so that the lanes of one LDS cycle hit
+// different banks.
+//
+// Selection is exact top-K with ties to the lower expert id, done in two
+// passes over the row instead of a K-step arg-max:
+//   pass 1 keeps the K largest values as a descending register list; a new
+//          value x enters as b[0] = max(b[0], x), b[i] = med3(b[i-1], b[i], x)
+//          (one instruction per slot, no index bookkeeping);
+//   pass 2 marks every expert whose logit is >= b[K-1] in a bit mask.
+// The mask has at least K bits; extra bits can only be ties with b[K-1], and
+// dropping those of the highest ids leaves the lower-id choice.  Slots are the
+// mask bits in ascending id order.  NaN logits (outside the contract) cannot
+// produce an invalid id: the mask is trimmed or filled to exactly K bits.
+template <int EB, int K>
+__global__ __launch_bounds__(256) void k1_route_map_stream(const float* __restrict__ logits,
+                                                           int64_t L, int E, int C, int64_t Lpad,
+                                                           int32_t* __restrict__ tei,
+                                                           float* __restrict__ gates,
+                                                           uint8_t* __restrict__ map,
+                                                           int32_t* __restrict__ tilecnt) {
+  using mask_t = typename MaskT<EB>::type;
+  constexpr int T = 256;
+  __shared__ __attribute__((aligned(16))) char stage[T * 4 * EB];  // 256 rows of 4 E bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smap[EB * T];     // [E][T] slot + 1
+  const int tile = blockIdx.x;
+  const int64_t t0 = (int64_t)tile * T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rowb = 4 * E;
+
+  {  // this wavefront's 64 rows are contiguous in memory
+    const int64_t first = (t0 + wave * 64) * rowb;
+    const int64_t total = L * rowb;
+    char* dst = stage + wave * 64 * rowb;
+    const int nq = E >> 2;  // 64 rows x 4 E bytes = E/4 transfers of 1 KB
+    for (int q = 0; q < nq; ++q) {
+      const int64_t off = first + q * 1024 + lane * 16;
+      const char* g = reinterpret_cast<const char*>(logits) + (off + 16 <= total ? off : 0);
+      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+    }
+  }
+  for (int i = threadIdx.x; i < (E * T) >> 4; i += 256)
+    reinterpret_cast<uint4*>(smap)[i] = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int tl = wave * 64 + lane;
+  const int64_t t = t0 + tl;
+  if (t < L) {
+    const float* row = reinterpret_cast<const float*>(stage + tl * rowb);
+    const int nc = E >> 2;
+    const int rot = lane % nc;
+
+    float b[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) b[i] = -INFINITY;
+    for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
+      const float4 q = reinterpret_cast<const float4*>(row)[c];
+      const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x = qv[u];
+#pragma unroll
+        for (int i = K - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], x);
+        b[0] = fmaxf(b[0], x);
+      }
+    }
+    const float thr = b[K - 1];
+
+    mask_t m = 0;
+    for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
+      const float4 q = reinterpret_cast<const float4*>(row)[c];
+      const mask_t m4 = (q.x >= thr ? 1u : 0u) | (q.y >= thr ? 2u : 0u) | (q.z >= thr ? 4u : 0u) |
+                        (q.w >= thr ? 8u : 0u);
+      m |= m4 << (4 * c);
+    }
+    int cnt = bit_count(m);
+    for (int e = E - 1; e >= 0 && cnt > K; --e) {
+      if (((m >> e) & 1) && !(row[e] > thr)) {
+        m &= ~((mask_t)1 << e);
+        --cnt;
+      }
+    }
+    for (int e = 0; e < E && cnt < K; ++e) {
+      if (!((m >> e) & 1)) {
+        m |= (mask_t)1 << e;
+        ++cnt;
+      }
+    }
+
+    const float vmax = b[0];
+    float ssum = 0.f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) ssum += expf(b[i] - vmax);
+    const float inv = 1.0f / ssum;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = lowest_bit(m);
+      m &= m - 1;
+      tei[t * K + k] = e;
+      gates[t * K + k] = expf(row[e] - vmax) * inv;
+      smap[e * T + tl] = (uint8_t)(k + 1);
+    }
+  }
+  __syncthreads();
+
+  const int nv = T >> 4;
+  for (int e = wave; e < E; e += 4) {
+    int cnt = 0;
+    for (int i = lane; i < nv; i += 64) {
+      const uint4 q = reinterpret_cast<const uint4*>(smap)[(e * T >> 4) + i];
+      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = q;
+      cnt += nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) tilecnt[(int64_t)e * C + tile] = cnt;
+  }
+}
+
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
 // row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
 // the row sum when total is not null.
@@ -337,14 +470,18 @@ void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, in
   hipLaunchKernelGGL(seg_scan, dim3(rows), dim3(256), 0, s, cnt, C, row_offset, base, total);
 }
 
+// The streaming routing kernel handles E <= 64 with E % 4 == 0 and K <= 8
+// (logits 16-byte aligned); it works on 256-token tiles.
+static bool stream_path(int E, int K) { return E <= 64 && E % 4 == 0 && K <= 8; }
+
 DispatchPlan plan_dispatch(int64_t L, int E, int K) {
-  (void)K;
   DispatchPlan p;
   // T is a power of two in [256, 1024] (the scatter kernel splits a
   // wavefront into T/16-lane row segments), with E * T <= 32 KB of LDS
   // where possible (E * T <= 64 KB always, since E <= 256).
   int T = 1024;
   while (T > 256 && E * T > 32768) T >>= 1;
+  if (stream_path(E, K)) T = 256;
   p.T = T;
   p.C = (int)((L + T - 1) / T);
   p.Lpad = (int64_t)p.C * T;
@@ -380,7 +517,31 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
     LaunchTimer lt("dispatch_route_map", s);
     const int q = (E + 3) / 4;  // lanes needed per token
     const bool rows_ok = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-    if (rows_ok && E <= 64) {
+    if (rows_ok && stream_path(E, K) && pl.T == 256) {
+#define K1S(EBV, KV)                                                                         \
+  hipLaunchKernelGGL((k1_route_map_stream<EBV, KV>), dim3(pl.C), dim3(256), 0, s, logits, L, E, \
+                     pl.C, pl.Lpad, tei, gates, map, cnt)
+#define K1S_K(EBV)                                                                           \
+  switch (K) {                                                                               \
+    case 1: K1S(EBV, 1); break;                                                              \
+    case 2: K1S(EBV, 2); break;                                                              \
+    case 3: K1S(EBV, 3); break;                                                              \
+    case 4: K1S(EBV, 4); break;                                                              \
+    case 5: K1S(EBV, 5); break;                                                              \
+    case 6: K1S(EBV, 6); break;                                                              \
+    case 7: K1S(EBV, 7); break;                                                              \
+    default: K1S(EBV, 8); break;                                                             \
+  }
+      if (E <= 16) {
+        K1S_K(16)
+      } else if (E <= 32) {
+        K1S_K(32)
+      } else {
+        K1S_K(64)
+      }
+#undef K1S_K
+#undef K1S
+    } else if (rows_ok && E <= 64) {
       const size_t sh = (size_t)E * pl.T;
 #define MOE_K1R(EVV)                                                                            \
   hipLaunchKernelGGL((k1_route_map_rows<EVV>), dim3(pl.C), dim3(256), sh, s, logits, L, E, K,   \
