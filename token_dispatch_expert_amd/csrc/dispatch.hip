@@ -244,152 +244,321 @@ __global__ __launch_bounds__(256) void k1_route_map_rows(const float* __restrict
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int EB> struct MaskT { using type = uint32_t; };
-template <> struct MaskT<64> { using type = uint64_t; };
-
-__device__ __forceinline__ int lowest_bit(uint32_t m) { return __builtin_ctz(m); }
 __device__ __forceinline__ int lowest_bit(uint64_t m) { return __builtin_ctzll(m); }
-__device__ __forceinline__ int bit_count(uint32_t m) { return __builtin_popcount(m); }
-__device__ __forceinline__ int bit_count(uint64_t m) { return __builtin_popcountll(m); }
 
-// Step 1, streaming form for E <= EB (E % 4 == 0, EB in {16, 32, 64}) and a
-// compile-time K <= 8: one tile of 256 tokens per workgroup, one token per
-// lane.  Each wavefront copies the 64 consecutive logit rows of its tokens
-// (one contiguous run of 256 E bytes) straight into LDS with 1 KB
-// global_load_lds transfers; each lane then reads its own row back, starting
-// at a lane-dependent 16-byte chunk so that the lanes of one LDS cycle hit
-// different banks.
+// Step 1, streaming form (E <= EB <= 64, K <= KM <= 8).  One wavefront per
+// workgroup routes one 64-token part, one token per lane (small workgroups
+// keep many parts in flight per CU).  The part's logit rows are one
+// contiguous run of 256 E bytes, copied straight into LDS with 1 KB
+// global_load_lds transfers (from the 16-byte boundary at or below its start,
+// so any 4-byte aligned logits work).  Each lane reads its own row back in
+// 4-element chunks, starting at a lane-dependent chunk so that the lanes of
+// one LDS cycle hit different banks.  VEC: E % 4 == 0 and 16-byte aligned
+// rows, read as float4.
 //
 // Selection is exact top-K with ties to the lower expert id, done in two
-// passes over the row instead of a K-step arg-max:
-//   pass 1 keeps the K largest values as a descending register list; a new
+// passes over the row instead of K arg-max passes:
+//   pass 1 keeps the KM largest values as a descending register list; a new
 //          value x enters as b[0] = max(b[0], x), b[i] = med3(b[i-1], b[i], x)
 //          (one instruction per slot, no index bookkeeping);
-//   pass 2 marks every expert whose logit is >= b[K-1] in a bit mask.
+//   pass 2 marks every expert whose logit is >= b[K-1] in a 64-bit mask.
 // The mask has at least K bits; extra bits can only be ties with b[K-1], and
 // dropping those of the highest ids leaves the lower-id choice.  Slots are the
 // mask bits in ascending id order.  NaN logits (outside the contract) cannot
 // produce an invalid id: the mask is trimmed or filled to exactly K bits.
-template <int EB, int K>
-__global__ __launch_bounds__(256) void k1_route_map_stream(const float* __restrict__ logits,
-                                                           int64_t L, int E, int C, int64_t Lpad,
-                                                           int32_t* __restrict__ tei,
-                                                           float* __restrict__ gates,
-                                                           uint8_t* __restrict__ map,
-                                                           int32_t* __restrict__ tilecnt) {
-  using mask_t = typename MaskT<EB>::type;
-  constexpr int T = 256;
-  __shared__ __attribute__((aligned(16))) char stage[T * 4 * EB];  // 256 rows of 4 E bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smap[EB * T];     // [E][T] slot + 1
-  const int tile = blockIdx.x;
-  const int64_t t0 = (int64_t)tile * T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rowb = 4 * E;
+//
+// Outputs besides tei and gates (the token-expert map of the method, in bit
+// form): each token's expert mask; for each part and expert e the wave
+// ballot col[part][e] (bit j set = token j of the part chose e); and the
+// part's per-expert counts cnt[e][part].
+// Transposes a wavefront's expert masks: for e in [E0, EB), lane e of
+// (hi:lo) receives the ballot of bit e of m (bit j = lane j has bit e set).
+template <int E0, int EB>
+struct BallotColumns {
+  static __device__ __forceinline__ void run(uint64_t m, uint32_t& lo, uint32_t& hi) {
+    const uint64_t bal = __ballot((m >> E0) & 1);
+    // the ballot was just written by a VALU compare: two wait states before
+    // it is read (the hazard checker does not look inside inline asm)
+    asm("s_nop 1\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
+        : "=v"(lo), "=v"(hi)
+        : "s"((uint32_t)bal), "s"((uint32_t)(bal >> 32)), "i"(E0), "0"(lo), "1"(hi));
+    BallotColumns<E0 + 1, EB>::run(m, lo, hi);
+  }
+};
+template <int EB>
+struct BallotColumns<EB, EB> {
+  static __device__ __forceinline__ void run(uint64_t, uint32_t&, uint32_t&) {}
+};
 
-  {  // this wavefront's 64 rows are contiguous in memory
-    const int64_t first = (t0 + wave * 64) * rowb;
-    const int64_t total = L * rowb;
-    char* dst = stage + wave * 64 * rowb;
-    const int nq = E >> 2;  // 64 rows x 4 E bytes = E/4 transfers of 1 KB
-    for (int q = 0; q < nq; ++q) {
-      const int64_t off = first + q * 1024 + lane * 16;
-      const char* g = reinterpret_cast<const char*>(logits) + (off + 16 <= total ? off : 0);
-      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+struct RouteSrc {
+  const char* abase;  // logits rounded down to 16 bytes
+  int64_t mis;        // logits - abase
+  int64_t end16;      // readable bytes from abase (rounded up to 16)
+};
+
+// Issue the copy of part `part` into `dst`; returns the offset of its first
+// row inside `dst`.
+__device__ __forceinline__ int copy_part(const RouteSrc& src, int64_t part, int rowb, int64_t L,
+                                         char* dst, int lane) {
+  const int64_t first = src.mis + part * 64 * rowb;
+  const int64_t first16 = first & ~(int64_t)15;
+  const int delta = (int)(first - first16);
+  const int nq = part * 64 < L ? (int)((delta + 64 * rowb + 1023) >> 10) : 0;
+  for (int q = 0; q < nq; ++q) {
+    const int64_t off = first16 + q * 1024 + lane * 16;
+    const char* g = src.abase + (off + 16 <= src.end16 ? off : 0);
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+  }
+  return delta;
+}
+
+template <int EB, int KM, bool VEC>
+__device__ __forceinline__ uint64_t route_row(const float* row, int E, int K, int lane, bool live,
+                                              int64_t t, int32_t* __restrict__ tei,
+                                              float* __restrict__ gates) {
+  const int nc = (E + 3) >> 2;
+  const int rot = lane % nc;
+  auto chunk = [&](int c, float (&v)[4]) {
+    if (VEC) {
+      const float4 q = reinterpret_cast<const float4*>(row)[c];
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (4 * c + u < E) ? row[4 * c + u] : -INFINITY;
+    }
+  };
+  float b[KM];
+#pragma unroll
+  for (int i = 0; i < KM; ++i) b[i] = -INFINITY;
+  for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
+    float v[4];
+    chunk(c, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int i = KM - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], v[u]);
+      b[0] = fmaxf(b[0], v[u]);
     }
   }
-  for (int i = threadIdx.x; i < (E * T) >> 4; i += 256)
-    reinterpret_cast<uint4*>(smap)[i] = make_uint4(0, 0, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  float thr = b[0];
+#pragma unroll
+  for (int i = 1; i < KM; ++i) thr = (i == K - 1) ? b[i] : thr;
 
-  const int tl = wave * 64 + lane;
-  const int64_t t = t0 + tl;
-  if (t < L) {
-    const float* row = reinterpret_cast<const float*>(stage + tl * rowb);
-    const int nc = E >> 2;
-    const int rot = lane % nc;
+  uint64_t m = 0;
+  for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
+    float v[4];
+    chunk(c, v);
+    const uint32_t m4 = (v[0] >= thr ? 1u : 0u) | (v[1] >= thr ? 2u : 0u) |
+                        (v[2] >= thr ? 4u : 0u) | (v[3] >= thr ? 8u : 0u);
+    m |= (uint64_t)m4 << (4 * c);
+  }
+  if (!VEC && E < 64) m &= (1ull << E) - 1;  // padding of the last chunk
+  int cnt = __builtin_popcountll(m);
+  for (int e = E - 1; e >= 0 && cnt > K; --e) {
+    if (((m >> e) & 1) && !(row[e] > thr)) {
+      m &= ~(1ull << e);
+      --cnt;
+    }
+  }
+  for (int e = 0; e < E && cnt < K; ++e) {
+    if (!((m >> e) & 1)) {
+      m |= 1ull << e;
+      ++cnt;
+    }
+  }
+  if (!live) return 0;
 
-    float b[K];
+  const float vmax = b[0];
+  float ssum = 0.f;
 #pragma unroll
-    for (int i = 0; i < K; ++i) b[i] = -INFINITY;
-    for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
-      const float4 q = reinterpret_cast<const float4*>(row)[c];
-      const float qv[4] = {q.x, q.y, q.z, q.w};
+  for (int i = 0; i < KM; ++i)
+    if (i < K) ssum += expf(b[i] - vmax);
+  const float inv = 1.0f / ssum;
+  uint64_t mm = m;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x = qv[u];
-#pragma unroll
-        for (int i = K - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], x);
-        b[0] = fmaxf(b[0], x);
-      }
-    }
-    const float thr = b[K - 1];
-
-    mask_t m = 0;
-    for (int j = 0, c = rot; j < nc; ++j, c = (c + 1 == nc) ? 0 : c + 1) {
-      const float4 q = reinterpret_cast<const float4*>(row)[c];
-      const mask_t m4 = (q.x >= thr ? 1u : 0u) | (q.y >= thr ? 2u : 0u) | (q.z >= thr ? 4u : 0u) |
-                        (q.w >= thr ? 8u : 0u);
-      m |= m4 << (4 * c);
-    }
-    int cnt = bit_count(m);
-    for (int e = E - 1; e >= 0 && cnt > K; --e) {
-      if (((m >> e) & 1) && !(row[e] > thr)) {
-        m &= ~((mask_t)1 << e);
-        --cnt;
-      }
-    }
-    for (int e = 0; e < E && cnt < K; ++e) {
-      if (!((m >> e) & 1)) {
-        m |= (mask_t)1 << e;
-        ++cnt;
-      }
-    }
-
-    const float vmax = b[0];
-    float ssum = 0.f;
-#pragma unroll
-    for (int i = 0; i < K; ++i) ssum += expf(b[i] - vmax);
-    const float inv = 1.0f / ssum;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int e = lowest_bit(m);
-      m &= m - 1;
+  for (int k = 0; k < KM; ++k) {
+    if (k < K) {
+      const int e = lowest_bit(mm);
+      mm &= mm - 1;
       tei[t * K + k] = e;
       gates[t * K + k] = expf(row[e] - vmax) * inv;
-      smap[e * T + tl] = (uint8_t)(k + 1);
+    }
+  }
+  return m;
+}
+
+template <int EB, int KM, bool VEC>
+__global__ __launch_bounds__(64) void k1_route_mask(const float* __restrict__ logits, int64_t L,
+                                                    int E, int K, int64_t NP,
+                                                    int32_t* __restrict__ tei,
+                                                    float* __restrict__ gates,
+                                                    uint64_t* __restrict__ tmask,
+                                                    uint64_t* __restrict__ tcol,
+                                                    int32_t* __restrict__ partcnt) {
+  constexpr int PART = 64 * 4 * EB + (VEC ? 0 : 1024);  // LDS bytes
+  __shared__ __attribute__((aligned(16))) char stage[PART];
+  const int lane = threadIdx.x;
+  const int64_t part = blockIdx.x;
+  const int rowb = 4 * E;
+  RouteSrc src;
+  {
+    const char* lbase = reinterpret_cast<const char*>(logits);
+    src.mis = (int64_t)(reinterpret_cast<uintptr_t>(lbase) & 15);  // 0 when VEC
+    src.abase = lbase - src.mis;
+    src.end16 = (src.mis + L * rowb + 15) & ~(int64_t)15;
+  }
+  const int delta = copy_part(src, part, rowb, L, stage, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int64_t t = part * 64 + lane;
+  const float* row = reinterpret_cast<const float*>(stage + delta + lane * rowb);
+  const uint64_t m = route_row<EB, KM, VEC>(row, E, K, lane, t < L, t, tei, gates);
+  if (t < L) tmask[t] = m;
+  // one ballot per expert: the part's column of the map, kept by lane e
+  // (bits of experts >= E are clear, so their ballots are empty)
+  uint32_t col_lo = 0, col_hi = 0;
+  BallotColumns<0, EB>::run(m, col_lo, col_hi);
+  const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+  if (lane < E) {
+    tcol[part * E + lane] = mycol;
+    partcnt[(int64_t)lane * NP + part] = __popcll(mycol);
+  }
+}
+
+// Step 3 for the streaming form: one workgroup per 256-token tile, one
+// wavefront per 64-token part.  A token's position in expert e's segment is
+// the segment start, plus the tokens of e in earlier tiles (scanned counts),
+// plus those in earlier parts of this tile, plus the set bits of the part's
+// column col[e] below its lane.  Tokens therefore appear in ascending order
+// within each segment, and the tile's tokens of one expert occupy one run of
+// that segment: the tile collects its entries in LDS ordered by expert and
+// writes them out run by run.  Tiles are spread over the XCDs in contiguous
+// ranges so that neighbouring runs meet in one L2.
+template <int RW>
+__global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restrict__ tmask,
+                                                       const uint64_t* __restrict__ tcol,
+                                                       int64_t L, int E, int K, int NU,
+                                                       const int32_t* __restrict__ unitbase,
+                                                       const int32_t* __restrict__ total,
+                                                       int32_t* __restrict__ eti,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ tim) {
+  constexpr int MAXE = 256 * 8;  // entries of one tile (K <= 8)
+  __shared__ int s_off[257];
+  __shared__ int scratch[4];
+  __shared__ uint64_t s_col[4][64];
+  __shared__ int s_ub[4][64];
+  __shared__ int s_base[4][64];
+  __shared__ int s_run[65];  // start of each expert's run inside the tile
+  __shared__ int s_tok[MAXE];
+  __shared__ int s_pos[MAXE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int tile;
+  {
+    const int nb = gridDim.x, b = blockIdx.x, q = nb >> 3, r = nb & 7, x = b & 7;
+    tile = x * q + (x < r ? x : r) + (b >> 3);
+  }
+  const int64_t part = (int64_t)tile * 4 + wave;
+  const int64_t t = part * 64 + lane;
+  const bool part_live = part * 64 < L;
+  const int64_t unit = part / RW;
+
+  // independent loads first
+  const int v = tid < E ? total[tid] : 0;
+  const uint64_t colv = (lane < E && part_live) ? tcol[part * E + lane] : 0;
+  const int ub = (lane < E && part_live && wave % RW == 0) ? unitbase[(int64_t)lane * NU + unit] : 0;
+  uint64_t m = t < L ? tmask[t] : 0;
+
+  int tot;
+  const int inc = block256_incl_scan(v, scratch, &tot);
+  if (tid < E) s_off[tid] = inc - v;
+  if (tid == 0) s_off[E] = tot;
+  if (lane < E) {
+    s_col[wave][lane] = colv;
+    s_ub[wave][lane] = ub;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) offsets[tid] = s_off[tid];
+    if (tid == 0) offsets[E] = s_off[E];
+  }
+  if (wave == 0) {
+    int run = 0, first = 0;
+    if (lane < E) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w % RW == 0) run = s_off[lane] + s_ub[w][lane];
+        if (w == 0) first = run;
+        s_base[w][lane] = run;
+        run += __popcll(s_col[w][lane]);
+      }
+    }
+    const int n = lane < E ? run - first : 0;  // this tile's tokens of expert lane
+    const int incl = wave_incl_scan(n, lane);
+    if (lane < E) s_run[lane] = incl - n;
+    if (lane == 63) s_run[64] = incl;
+  }
+  __syncthreads();
+  if (t < L) {
+    for (int k = 0; k < K && m != 0; ++k) {
+      const int e = lowest_bit(m);
+      m &= m - 1;
+      const uint64_t ce = s_col[wave][e];
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ce >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ce, 0));
+      const int pos = s_base[wave][e] + below;
+      const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
+      if (lp < MAXE) {  // always true when the masks hold K bits each
+        s_tok[lp] = (int32_t)t;
+        s_pos[lp] = pos;
+      }
+      tim[t * K + k] = pos;
     }
   }
   __syncthreads();
-
-  const int nv = T >> 4;
-  for (int e = wave; e < E; e += 4) {
-    int cnt = 0;
-    for (int i = lane; i < nv; i += 64) {
-      const uint4 q = reinterpret_cast<const uint4*>(smap)[(e * T >> 4) + i];
-      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = q;
-      cnt += nonzero_bytes(q.x) + nonzero_bytes(q.y) + nonzero_bytes(q.z) + nonzero_bytes(q.w);
-    }
-    cnt = wave_sum(cnt);
-    if (lane == 0) tilecnt[(int64_t)e * C + tile] = cnt;
+  const int n = min(s_run[64], MAXE);
+  const int64_t R = L * K;
+  for (int j = tid; j < n; j += 256) {
+    const int pos = s_pos[j];
+    if (pos < R) eti[pos] = s_tok[j];  // always true when the masks hold K bits each
   }
 }
 
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
 // row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
-// the row sum when total is not null.
+// the row sum when total is not null.  With G > 1 the input rows hold G
+// consecutive counts per entry ([rows][C * G]), which are added first.
+template <int G>
 __global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt, int C,
                                                 int64_t row_offset, int32_t* __restrict__ base,
                                                 int32_t* __restrict__ total) {
+  constexpr int V = 16;  // consecutive entries per thread and pass
   __shared__ int scratch[4];
   const int r = blockIdx.x;
+  const int32_t* in = cnt + (int64_t)r * C * G;
+  int32_t* out = base + (int64_t)r * C;
   int run = 0;
-  for (int c0 = 0; c0 < C; c0 += 256) {
-    const int c = c0 + threadIdx.x;
-    const int v = c < C ? cnt[(int64_t)r * C + c] : 0;
+  for (int c0 = 0; c0 < C; c0 += 256 * V) {
+    const int cb = c0 + threadIdx.x * V;
+    int x[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      x[i] = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[i] += cb + i < C ? in[(int64_t)(cb + i) * G + g] : 0;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) sum += x[i];
     int tot;
-    const int inc = block256_incl_scan(v, scratch, &tot);
-    if (c < C) base[(int64_t)r * C + c] = (int32_t)(r * row_offset + run + inc - v);
+    int ex = block256_incl_scan(sum, scratch, &tot) - sum;
+    const int64_t add = r * row_offset + run;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (cb + i < C) out[cb + i] = (int32_t)(add + ex);
+      ex += x[i];
+    }
     run += tot;
   }
   if (total != nullptr && threadIdx.x == 0) total[r] = run;
@@ -467,27 +636,38 @@ __global__ __launch_bounds__(256) void k3_scatter(const uint8_t* __restrict__ ma
 
 void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, int32_t* base,
                      int32_t* total, hipStream_t s) {
-  hipLaunchKernelGGL(seg_scan, dim3(rows), dim3(256), 0, s, cnt, C, row_offset, base, total);
+  hipLaunchKernelGGL(seg_scan<1>, dim3(rows), dim3(256), 0, s, cnt, C, row_offset, base, total);
 }
 
-// The streaming routing kernel handles E <= 64 with E % 4 == 0 and K <= 8
-// (logits 16-byte aligned); it works on 256-token tiles.
-static bool stream_path(int E, int K) { return E <= 64 && E % 4 == 0 && K <= 8; }
+// The streaming kernels (bit-mask map, 256-token tiles) serve E <= 64 and
+// K <= 8; larger E or K use the byte map with 256..1024-token tiles.
+static bool stream_path(int E, int K) { return E <= 64 && K <= 8; }
 
 DispatchPlan plan_dispatch(int64_t L, int E, int K) {
   DispatchPlan p;
-  // T is a power of two in [256, 1024] (the scatter kernel splits a
-  // wavefront into T/16-lane row segments), with E * T <= 32 KB of LDS
-  // where possible (E * T <= 64 KB always, since E <= 256).
-  int T = 1024;
-  while (T > 256 && E * T > 32768) T >>= 1;
-  if (stream_path(E, K)) T = 256;
+  p.stream = stream_path(E, K);
+  int T;
+  if (p.stream) {
+    T = 256;
+  } else {
+    // T is a power of two in [256, 1024] (the scatter kernel splits a
+    // wavefront into T/16-lane row segments), with E * T <= 32 KB of LDS
+    // where possible (E * T <= 64 KB always, since E <= 256).
+    T = 1024;
+    while (T > 256 && E * T > 32768) T >>= 1;
+  }
   p.T = T;
   p.C = (int)((L + T - 1) / T);
   p.Lpad = (int64_t)p.C * T;
+  // every part of every 256-token tile is routed (parts past L write zero
+  // counts), so the grouped scan reads only written entries
+  p.NP = p.stream ? (int64_t)4 * p.C : 0;
+  // map: one 64-bit expert mask per token (stream) or the [E][Lpad] byte map
+  const size_t map_bytes = p.stream ? (size_t)8 * p.Lpad : (size_t)E * p.Lpad;
   size_t o = 0;
-  p.off_map = o;   o = align_up(o + (size_t)E * p.Lpad, 256);
-  p.off_cnt = o;   o = align_up(o + (size_t)E * p.C * 4, 256);
+  p.off_map = o;   o = align_up(o + map_bytes, 256);
+  p.off_col = o;   o = align_up(o + (p.stream ? (size_t)8 * E * (p.Lpad / 64) : 0), 256);
+  p.off_cnt = o;   o = align_up(o + (size_t)E * (p.stream ? 4 * p.C : p.C) * 4, 256);
   p.off_base = o;  o = align_up(o + (size_t)E * p.C * 4, 256);
   p.off_total = o; o = align_up(o + 256 * 4, 256);
   p.bytes = o;
@@ -506,6 +686,7 @@ static void launch_k1(const DispatchPlan& pl, int64_t L, int E, int K, const flo
                        logits, L, E, K, pl.T, pl.C, pl.Lpad, tei, gates, map, cnt);
 }
 
+
 hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, const float* logits,
                            int32_t* eti, int32_t* offsets, int32_t* tei, int32_t* tim,
                            float* gates, char* ws, hipStream_t s) {
@@ -517,30 +698,36 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
     LaunchTimer lt("dispatch_route_map", s);
     const int q = (E + 3) / 4;  // lanes needed per token
     const bool rows_ok = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-    if (rows_ok && stream_path(E, K) && pl.T == 256) {
-#define K1S(EBV, KV)                                                                         \
-  hipLaunchKernelGGL((k1_route_map_stream<EBV, KV>), dim3(pl.C), dim3(256), 0, s, logits, L, E, \
-                     pl.C, pl.Lpad, tei, gates, map, cnt)
-#define K1S_K(EBV)                                                                           \
-  switch (K) {                                                                               \
-    case 1: K1S(EBV, 1); break;                                                              \
-    case 2: K1S(EBV, 2); break;                                                              \
-    case 3: K1S(EBV, 3); break;                                                              \
-    case 4: K1S(EBV, 4); break;                                                              \
-    case 5: K1S(EBV, 5); break;                                                              \
-    case 6: K1S(EBV, 6); break;                                                              \
-    case 7: K1S(EBV, 7); break;                                                              \
-    default: K1S(EBV, 8); break;                                                             \
+    if (pl.stream) {
+      uint64_t* tmask = reinterpret_cast<uint64_t*>(ws + pl.off_map);
+      uint64_t* tcol = reinterpret_cast<uint64_t*>(ws + pl.off_col);
+#define K1M(EBV, KV, VV)                                                                        \
+  hipLaunchKernelGGL((k1_route_mask<EBV, KV, VV>), dim3(pl.NP), dim3(64), 0, s, logits, L, E, K, \
+                     pl.NP, tei, gates, tmask, tcol, cnt)
+#define K1M_K(EBV)                                                                              \
+  if (!rows_ok) {                                                                               \
+    K1M(EBV, 8, false);                                                                         \
+  } else {                                                                                      \
+    switch (K) {                                                                                \
+      case 1: K1M(EBV, 1, true); break;                                                         \
+      case 2: K1M(EBV, 2, true); break;                                                         \
+      case 3: K1M(EBV, 3, true); break;                                                         \
+      case 4: K1M(EBV, 4, true); break;                                                         \
+      case 5: K1M(EBV, 5, true); break;                                                         \
+      case 6: K1M(EBV, 6, true); break;                                                         \
+      case 7: K1M(EBV, 7, true); break;                                                         \
+      default: K1M(EBV, 8, true); break;                                                        \
+    }                                                                                           \
   }
       if (E <= 16) {
-        K1S_K(16)
+        K1M_K(16)
       } else if (E <= 32) {
-        K1S_K(32)
+        K1M_K(32)
       } else {
-        K1S_K(64)
+        K1M_K(64)
       }
-#undef K1S_K
-#undef K1S
+#undef K1M_K
+#undef K1M
     } else if (rows_ok && E <= 64) {
       const size_t sh = (size_t)E * pl.T;
 #define MOE_K1R(EVV)                                                                            \
@@ -561,12 +748,22 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
   }
   {
     LaunchTimer lt("dispatch_expert_scan", s);
-    launch_seg_scan(cnt, E, pl.C, 0, base, total, s);
+    if (pl.stream)  // per-part counts, added four at a time into 256-token tiles
+      hipLaunchKernelGGL(seg_scan<4>, dim3(E), dim3(256), 0, s, cnt, pl.C, (int64_t)0, base,
+                         total);
+    else
+      launch_seg_scan(cnt, E, pl.C, 0, base, total, s);
   }
   {
     LaunchTimer lt("dispatch_scatter", s);
-    hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
-                       base, total, eti, offsets, tim);
+    if (pl.stream)
+      hipLaunchKernelGGL(k3_scatter_mask<4>, dim3(pl.C), dim3(256), 0, s,
+                         reinterpret_cast<const uint64_t*>(ws + pl.off_map),
+                         reinterpret_cast<const uint64_t*>(ws + pl.off_col), L, E, K, pl.C, base,
+                         total, eti, offsets, tim);
+    else
+      hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
+                         base, total, eti, offsets, tim);
   }
   return hipGetLastError();
 }

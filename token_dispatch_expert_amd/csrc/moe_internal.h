@@ -27,7 +27,9 @@ struct DispatchPlan {
   int T;          // tokens per tile
   int C;          // tiles
   int64_t Lpad;   // C * T (row length of the token-expert map)
-  size_t off_map, off_cnt, off_base, off_total, bytes;
+  bool stream;    // bit-mask map (E <= 64, K <= 8)
+  int64_t NP;     // 64-token parts of the streaming router (per-part counts)
+  size_t off_map, off_col, off_cnt, off_base, off_total, bytes;
 };
 DispatchPlan plan_dispatch(int64_t L, int E, int K);
 hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, const float* logits,
