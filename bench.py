@@ -53,11 +53,26 @@ def kernel_flops(cfg):
 
 
 def dispatch_bytes(cfg):
-    """Algorithmic HBM bytes of one dispatch build: logits read (4LE), the
-    uint8 token-expert map written once and read once (2LE), the four L*K
-    int32/float32 outputs token_expert_indices, gates, expert_token_indices,
-    token_index_map (16LK), and the offsets."""
-    return 4 * cfg.L * cfg.E + 2 * cfg.L * cfg.E + 16 * cfg.L * cfg.K + 4 * (cfg.E + 1)
+    """Algorithmic HBM bytes of one dispatch build, for the map representation
+    the library uses at this shape.
+
+    Always: logits read once (4LE), the four L*K int32/float32 outputs
+    token_expert_indices, gates, expert_token_indices, token_index_map written
+    once (16LK), and the offsets (4(E+1)).
+    E <= 64 and K <= 8 (bit-mask map): each token's 64-bit expert mask and each
+    64-token part's per-expert column (E/8 bytes per token) written once and
+    read once; per-part counts (int32 per expert and part) written and read,
+    256-token tile bases written and read.
+    Otherwise (byte map): E bytes per token written once and read once."""
+    L, E, K = cfg.L, cfg.E, cfg.K
+    b = 4 * L * E + 16 * L * K + 4 * (E + 1)
+    if E <= 64 and K <= 8:
+        tiles = -(-L // 256)
+        parts = 4 * tiles
+        b += 2 * 8 * L + 2 * 8 * E * parts + 2 * 4 * E * parts + 2 * 4 * E * tiles
+    else:
+        b += 2 * L * E
+    return b
 
 
 def source_hash():
@@ -75,8 +90,8 @@ ROCPROF_NAMES = {   # library timer name -> kernel symbol base name in rocprofv3
     "ffn_b0_dw2": "b0_dw2",
     "ffn_b2_dw13": "b2_dw13",
     "ffn_b3_dx": "b3_dx",
-    "dispatch_route_map": "k1_route_map",
-    "dispatch_scatter": "k3_scatter",
+    "dispatch_route_map": "k1_route_mask",     # E <= 64, K <= 8 (the byte-map path is k1_route_map*)
+    "dispatch_scatter": "k3_scatter_mask",
 }
 
 

@@ -19,20 +19,22 @@
 // workgroup; eight wavefronts (two per SIMD) in a 2 x 4 grid, each owning
 // 128 x 64 = 4 x 2 MFMA 32x32 tiles (bf16: v_mfma_f32_32x32x16_bf16;
 // float32: four v_mfma_f32_32x32x2f32 per 8-element k group).  One k-tile is
-// 128 bytes of k per row (64 bf16 / 32 float32).  Both operands sit in LDS
-// with k contiguous per row; the eight 16-byte chunks of a row are XOR-
-// swizzled by the row index so that fragment reads, row copies and the
-// transposed writes below do not collide on banks.  LDS is double buffered
-// (128 KB) and the next k-tile's global loads are issued before the current
-// tile's MFMAs.  Loads never branch: out-of-range rows or k read a valid
-// address and are zeroed by a select.
+// 128 bytes of k per row (64 bf16 / 32 float32).  Operands are copied from
+// global memory straight into LDS (global_load_lds, 16 bytes per lane), the
+// next k-tile's copies issued before the current tile's MFMAs; LDS is double
+// buffered (128 KB).  MFMA fragments for k-chunk kc + 1 are read while the
+// MFMAs of chunk kc issue.  Loads never branch: out-of-range rows or k read
+// a zero page instead.
 //
 // Operand layouts.  The forward products use weights transposed once per
 // call into the workspace (W1, W3 -> [E, h, d]; W2 -> [E, d, h]), so every
-// operand of F1, F2, B1 and B3 has k contiguous and is copied with 16-byte
-// row loads.  The weight-gradient products B0 and B2 reduce over routes, so
-// both of their operands have the M/N index contiguous; those are loaded as
-// 4 k-rows x 16 bytes and transposed in registers on the way into LDS.
+// operand of F1, F2, B1 and B3 has k contiguous: LDS rows are [position][k]
+// with the eight 16-byte chunks of a row XOR-swizzled by the row index, so
+// that fragment reads and row copies do not collide on banks.  The
+// weight-gradient products B0 and B2 reduce over routes, so both of their
+// operands have the M/N index contiguous: bf16 tiles stay [k][position] in
+// LDS and MFMA fragments come from the transposing LDS read
+// (ds_read_b64_tr_b16); float32 tiles are transposed in registers.
 //
 // Determinism: every output element has one writer.  The combine into y
 // and the input gradient dx run as K ordered slot passes: pass k handles,
@@ -82,36 +84,6 @@ __device__ __forceinline__ uint4 sel16(bool ok, uint4 v) {
 
 // ------------------------------------------------------------------ loaders
 
-// 256 rows with k contiguous in memory.  Thread owns rows (tid >> 3) + 64 i
-// (i < 4) and 16-byte chunk (tid & 7) of each k-tile.  Element k of row i is
-// at p0[i] + k (k < ksplit) or p0[i] + delta + (k - ksplit) (k >= ksplit):
-// the second source has the same row layout at a fixed byte distance.
-// Rows that are out of range point at a valid row and are zeroed.
-template <typename T>
-struct KLoader {
-  static constexpr bool kDirect = false;
-  const char* p0[4];
-  uint32_t valid;
-  int64_t delta;
-  int ksplit, klen;
-  uint4 reg[4];
-
-  __device__ __forceinline__ void fetch(int kt) {
-    constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
-    const int k = kt * KT + (threadIdx.x & 7) * VEC;
-    const bool inK = k < klen;
-    const int64_t o = !inK ? 0 : (k < ksplit ? (int64_t)k * ES : delta + (int64_t)(k - ksplit) * ES);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      reg[i] = sel16(inK && ((valid >> i) & 1u), *reinterpret_cast<const uint4*>(p0[i] + o));
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + lds_off(r + 64 * i, c)) = reg[i];
-  }
-};
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 16 bytes per lane straight from global memory into LDS: lane i of the
@@ -120,8 +92,11 @@ __device__ __forceinline__ void load_to_lds(const void* g, char* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-// Direct-to-LDS version of KLoader (same tile and swizzle).  Wavefront w
-// fills rows w*32 .. w*32+31 with four 1 KB loads; in load j lane l writes
+// 256 rows with k contiguous in memory, copied straight into LDS.  Element k
+// of a row is at its start + k (k < ksplit) or start + delta + (k - ksplit)
+// (k >= ksplit): the second source has the same row layout at a fixed byte
+// distance.  Wavefront w fills rows w*32 .. w*32+31 with four 1 KB loads; in
+// load j lane l writes
 // LDS row w*32 + 8 j + (l >> 3), physical chunk l & 7, so it fetches the
 // logical chunk (l & 7) ^ swizzle(row) of that row.  Absent rows and k
 // beyond klen read the zero page instead.
@@ -179,40 +154,14 @@ __device__ __forceinline__ void kloaderd_rows(KLoaderD<T>& la, const T* base, co
   }
 }
 
-// Row pointers of a KLoader: LDS row j of the tile is list entry rb + j
-// (the identity list when list == nullptr), optionally mapped through
-// `gather`; row index idx lives at base + idx * row_elems.  Entries at or
-// past `re` are invalid.
-template <typename T>
-__device__ __forceinline__ void kloader_rows(KLoader<T>& la, const T* base, const int32_t* list,
-                                             const int32_t* gather, int rb, int re,
-                                             int64_t row_elems) {
-  const int r = threadIdx.x >> 3;
-  la.valid = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int li = rb + r + 64 * i;
-    const bool ok = li < re;
-    int64_t idx = 0;
-    if (ok) {
-      idx = list != nullptr ? (int64_t)list[li] : (int64_t)li;
-      if (gather != nullptr) idx = gather[idx];
-    }
-    la.p0[i] = reinterpret_cast<const char*>(base + idx * row_elems);
-    la.valid |= (ok ? 1u : 0u) << i;
-  }
-}
-
-// 256 M/N positions with that index contiguous in memory, k indexing rows.
-// Row r(k) = ridx ? ridx[k] : rbase + k; the thread's 16-byte vector for
-// k-row k is at col + r(k) * ld.
-//   bf16:    thread t owns positions (t >> 4) * 8 .. +8 and k-rows
-//            ((t >> 1) & 7) * 8 + (t & 1) * 4 + i, i < 4 (half of a 16-byte
-//            k chunk); it writes 8 position rows x 8 bytes.
-//   float32: thread t owns positions (t >> 3) * 4 .. +4 and k-rows
-//            (t & 7) * 4 + i, i < 4 (a whole chunk); it writes 4 rows x 16 B.
-// Odd position groups write their rows in pair-swapped order so that
-// consecutive lanes cover both row parities of an LDS cycle.
+// float32 operand of the weight-gradient products: 256 M/N positions with
+// that index contiguous in memory, k indexing rows, transposed in registers
+// on its way into the [position][k] LDS tile.  Row r(k) = ridx ? ridx[k] :
+// rbase + k; the thread's 16-byte vector for k-row k is at col + r(k) * ld.
+// Thread t owns positions (t >> 3) * 4 .. +4 and k-rows (t & 7) * 4 + i,
+// i < 4 (a whole chunk); it writes 4 rows x 16 B.  Odd position groups write
+// their rows in pair-swapped order so that consecutive lanes cover both row
+// parities of an LDS cycle.  (bf16 uses TLoaderD.)
 template <typename T>
 struct MNLoader {
   static constexpr bool kDirect = false;
@@ -250,8 +199,8 @@ struct MNLoader {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + i;
-      const int kk = (colok && k < klen) ? k : 0;
-      rr[i] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
+      const bool in = colok && k < klen;  // the index array is never read past klen
+      rr[i] = ridx != nullptr ? (in ? (int64_t)ridx[k] : 0) : rbase + (in ? k : 0);
     }
   }
   __device__ __forceinline__ void prime() { rows_of(0, rnext); }
@@ -272,38 +221,9 @@ struct MNLoader {
 };
 
 template <>
-__device__ __forceinline__ int MNLoader<bf16_t>::pos0() { return (threadIdx.x >> 4) * 8; }
-template <>
-__device__ __forceinline__ int MNLoader<bf16_t>::krow0() {
-  return ((threadIdx.x >> 1) & 7) * 8 + (threadIdx.x & 1) * 4;
-}
-template <>
 __device__ __forceinline__ int MNLoader<float>::pos0() { return (threadIdx.x >> 3) * 4; }
 template <>
 __device__ __forceinline__ int MNLoader<float>::krow0() { return (threadIdx.x & 7) * 4; }
-
-template <>
-__device__ __forceinline__ void MNLoader<bf16_t>::store(char* lds) const {
-  const int c = (threadIdx.x >> 1) & 7, half = (threadIdx.x & 1) * 8;
-  const int n0 = pos0(), odd = (threadIdx.x >> 4) & 1;
-  const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&reg[0]);
-  const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&reg[1]);
-  const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&reg[2]);
-  const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&reg[3]);
-  uint2 out[8];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    out[2 * w].x = (q0[w] & 0xffffu) | (q1[w] << 16);
-    out[2 * w].y = (q2[w] & 0xffffu) | (q3[w] << 16);
-    out[2 * w + 1].x = (q0[w] >> 16) | (q1[w] & 0xffff0000u);
-    out[2 * w + 1].y = (q2[w] >> 16) | (q3[w] & 0xffff0000u);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint2 v = odd ? out[j ^ 1] : out[j];
-    *reinterpret_cast<uint2*>(lds + lds_off(n0 + (j ^ odd), c) + half) = v;
-  }
-}
 
 template <>
 __device__ __forceinline__ void MNLoader<float>::store(char* lds) const {
@@ -325,8 +245,7 @@ __device__ __forceinline__ void MNLoader<float>::store(char* lds) const {
 
 // bf16 operand tile kept as it lies in memory: 64 k-rows x 256 positions
 // (512 bytes per k-row).  MFMA fragments are read with the transposing LDS
-// read (ds_read_b64_tr_b16), so no register transpose is needed.  Thread t
-// copies 16-byte chunk (t & 31) of k-rows (t >> 5) + 16 i, i < 4.  The 32
+// read (ds_read_b64_tr_b16), so no register transpose is needed.  The 32
 // chunks of a k-row are XOR-swizzled by 4 * (k & 3), so that the four k-rows
 // read together by a 16-lane group of the transposing read fall on
 // different banks.
@@ -334,58 +253,7 @@ __device__ __forceinline__ int tlds_off(int k, int chunk) {
   return k * 512 + ((chunk ^ ((k & 3) << 2)) << 4);
 }
 
-struct TLoader {
-  static constexpr bool kDirect = false;
-  const char* col;        // byte address of position 0 of row 0 for this thread's chunk
-  bool colok;
-  int64_t ld;
-  const int32_t* ridx;
-  int64_t rbase;
-  int klen;
-  int64_t rnext[4];
-  uint4 reg[4];
-
-  __device__ static __forceinline__ int krow0() { return threadIdx.x >> 5; }
-
-  __device__ __forceinline__ void setup(const char* base, int first_pos, int limit, int64_t ld_,
-                                        const int32_t* ridx_, int64_t rbase_, int klen_) {
-    const int p = first_pos + (threadIdx.x & 31) * 8;
-    colok = p < limit;
-    col = base + (int64_t)(colok ? p : 0) * 2;
-    ld = ld_;
-    ridx = ridx_;
-    rbase = rbase_;
-    klen = klen_;
-    rows_of(0, rnext);
-  }
-  __device__ __forceinline__ void rows_of(int kt, int64_t (&rr)[4]) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = kt * 64 + krow0() + 16 * i;
-      const int kk = (colok && k < klen) ? k : 0;
-      rr[i] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
-    }
-  }
-  __device__ __forceinline__ void fetch(int kt) {
-    int64_t r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = rnext[i];
-    rows_of(kt + 1, rnext);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = colok && kt * 64 + krow0() + 16 * i < klen;
-      reg[i] = sel16(ok, *reinterpret_cast<const uint4*>(col + r[i] * ld));
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int c = threadIdx.x & 31;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(lds + tlds_off(krow0() + 16 * i, c)) = reg[i];
-  }
-};
-
-// Direct-to-LDS version of TLoader (same tile and swizzle).  Wavefront w
+// Loader of such a tile straight into LDS.  Wavefront w
 // fills k-rows w*8 .. w*8+7 with four 1 KB loads; in load j lane l writes
 // k-row w*8 + 2 j + (l >> 5), physical chunk l & 31, so it fetches logical
 // chunk (l & 31) ^ (4 (k & 3)) = positions 8 c .. 8 c + 7.
@@ -416,8 +284,8 @@ struct TLoaderD {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = kt * 64 + krow(j);
-      const int kk = k < klen ? k : 0;
-      rr[j] = ridx != nullptr ? (int64_t)ridx[kk] : rbase + kk;
+      const bool in = k < klen;  // the index array is never read past klen
+      rr[j] = ridx != nullptr ? (in ? (int64_t)ridx[k] : 0) : rbase + (in ? k : 0);
     }
   }
   __device__ __forceinline__ void issue(int kt, char* lds) {
@@ -438,7 +306,7 @@ struct TLoaderD {
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // Fragment of 32 positions p0 .. p0+31 and k = kbase .. kbase+15 from a
-// TLoader tile: lane l gets position p0 + (l & 31) and the 8 k values
+// TLoaderD tile: lane l gets position p0 + (l & 31) and the 8 k values
 // kbase + 8 (l >> 5) + 0..7, from two transposing reads of 4 k-rows each.
 // (Within a 16-lane group the read hands lane i element i & 3 of the
 // 8-byte chunk addressed by lane 4 m + (i >> 2), for m = 0..3.)
@@ -523,7 +391,7 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
   }
 }
 
-// One k-tile of MFMAs on two TLoader tiles (bf16).
+// One k-tile of MFMAs on two TLoaderD tiles (bf16).
 __device__ __forceinline__ void mma_ktile_tr(const char* As, const char* Bs, Acc& acc) {
   const int wm = wave_m(), wn = wave_n();
   uint4 a[2][MT], b[2][NTL];
@@ -550,7 +418,7 @@ __device__ __forceinline__ void mma_ktile_tr(const char* As, const char* Bs, Acc
 }
 
 // Main loop over nk k-tiles; result in acc (zero when nk == 0).  TR: both
-// operands are TLoader tiles read with the transposing LDS read.
+// operands are TLoaderD tiles read with the transposing LDS read.
 template <typename T, class LA, class LB, bool TR = false>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
 #pragma unroll
