@@ -24,7 +24,11 @@ layer, written out with numpy in float64:
 * the backward that scatters the (L, d) output gradient through the same
   indices, recomputes SiLU from the checkpointed first-MLP outputs and
   accumulates input and weight gradients (same sub-section, "Backward"
-  paragraph, and the activation-checkpoint paragraph).
+  paragraph, and the activation-checkpoint paragraph);
+* the gradient with respect to the router logits.  The pages do not describe
+  it; it is the derivative of the same forward (gates = softmax over the
+  selected logits) with respect to the logits, the selection itself being
+  piecewise constant.
 
 The MoEBlaze method reaches exactly this result (it is dropless and only
 changes how the work is laid out), so the oracle is the definition itself,
@@ -62,9 +66,11 @@ __all__ = [
     "build_indices",
     "ffn_forward",
     "ffn_backward",
+    "router_backward",
     "route_rows_forward",
     "token_rows",
     "dw_columns",
+    "router_rows",
     "checkpoint_bytes",
 ]
 
@@ -258,6 +264,43 @@ def ffn_backward(dy, x, W1, W3, W2, eti, offsets, tim, gates, act):
     return dx, dW1, dW3, dW2
 
 
+def _softmax_backward(gates, dgate):
+    """d(logit) of the selected experts from d(gate): for a softmax over the
+    selected logits, dz_k = g_k * (dg_k - sum_j g_j dg_j)."""
+    s = (gates * dgate).sum(axis=1, keepdims=True)
+    return gates * (dgate - s)
+
+
+def router_backward(dy, x, W1, W3, W2, eti, offsets, tei, tim, gates, act):
+    """Gradient of <y, dy> with respect to the router logits, float64 [L, E].
+
+    y[t] = sum_k g[t, k] O[tim[t, k]] with O = G W2[e] (the un-gated expert
+    output of the route), so d<y, dy>/dg[t, k] = <dy[t], O[tim[t, k]]>; the
+    gates are a softmax over the K selected logits (reading 2), whose
+    backward gives the selected logits' gradient; every other logit gets 0.
+    """
+    dy = _f64(dy); x = _f64(x); W1 = _f64(W1); W3 = _f64(W3); W2 = _f64(W2)
+    gates = np.asarray(gates, dtype=np.float64)
+    L, d = x.shape
+    E = W1.shape[0]
+    K = tim.shape[1]
+    O = np.zeros((L * K, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        X = x[eti[lo:hi]]
+        Ae = X @ W1[e]
+        Be = X @ W3[e] if act == SWIGLU else None
+        O[lo:hi] = _glu(Ae, Be, act) @ W2[e]
+    dgate = np.zeros((L, K))
+    for k in range(K):
+        dgate[:, k] = (dy * O[tim[:, k]]).sum(axis=1)
+    dz = np.zeros((L, E))
+    np.put_along_axis(dz, np.asarray(tei, dtype=np.int64), _softmax_backward(gates, dgate), axis=1)
+    return dz
+
+
 # ---------------------------------------------------------------------------
 # Sampled evaluation for shapes too large to run whole on the host.
 # Each function computes the same quantities as ffn_forward / ffn_backward
@@ -356,6 +399,26 @@ def dw_columns(e, cols, dy, x, W1, W3, W2, eti, offsets, tim, tei, gates, act):
         dAc = dGc * _dsilu(Ac)
         dW1c[:] = X.T @ dAc
     return dW1c, dW3c, dW2r
+
+
+def router_rows(tokens, dy, x, W1, W3, W2, tei, gates, act, E):
+    """Rows of router_backward (float64 [len(tokens), E]) for the listed
+    tokens: a token's logit gradient needs only its own K routes."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    K = tei.shape[1]
+    dz = np.zeros((tokens.size, E))
+    for i, t in enumerate(tokens):
+        xt = np.asarray(x[t], dtype=np.float64)
+        dyt = np.asarray(dy[t], dtype=np.float64)
+        dg = np.zeros((1, K))
+        for k in range(K):
+            e = int(tei[t, k])
+            a = xt @ np.asarray(W1[e], dtype=np.float64)
+            b = xt @ np.asarray(W3[e], dtype=np.float64) if act == SWIGLU else None
+            dg[0, k] = dyt @ (_glu(a, b, act) @ np.asarray(W2[e], dtype=np.float64))
+        g = np.asarray(gates[t], dtype=np.float64)[None, :]
+        dz[i, np.asarray(tei[t], dtype=np.int64)] = _softmax_backward(g, dg)[0]
+    return dz
 
 
 def checkpoint_bytes(L, K, h, act, elem_bytes):

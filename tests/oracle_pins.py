@@ -12,7 +12,11 @@ mistake) and raises AssertionError when the oracle disagrees with:
   float64, differentiated by torch autograd (library routine, CPU only),
 * the E = K = 1 case, which is a plain two-layer MLP (torch's SiLU),
 * float64 central finite differences of <y, dy>,
-* consistency of the sampled evaluators with the full forward/backward.
+* consistency of the sampled evaluators with the full forward/backward;
+* for the router-logit gradient: torch autograd of the dense formulation with
+  respect to the logits, float64 central finite differences of <y, dy> along
+  logit directions that keep the selection, the K = 1 case (gates are 1, so
+  the gradient is exactly 0) and the zero row sum of a softmax Jacobian.
 """
 
 from __future__ import annotations
@@ -103,8 +107,8 @@ def rank_mask(Z, K):
 def dense_mask_torch(logits, x, W1, W3, W2, dy, K, act):
     """Dense formulation: every expert on every token, weighted by a gate that
     is zero for unselected experts; gradients by torch autograd (float64)."""
-    Z = torch.tensor(np.asarray(logits, dtype=np.float64))
-    mask = rank_mask(Z, K)
+    Z = torch.tensor(np.asarray(logits, dtype=np.float64), requires_grad=True)
+    mask = rank_mask(Z.detach(), K)
     gate = torch.softmax(torch.where(mask, Z, torch.full_like(Z, -math.inf)), dim=1)
     xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
     w1 = torch.tensor(W1, dtype=torch.float64, requires_grad=True)
@@ -118,7 +122,7 @@ def dense_mask_torch(logits, x, W1, W3, W2, dy, K, act):
     (y * torch.tensor(dy, dtype=torch.float64)).sum().backward()
     out = dict(y=y.detach().numpy(), dx=xt.grad.numpy(), dW1=w1.grad.numpy(),
                dW2=w2.grad.numpy(), dW3=None if w3 is None else w3.grad.numpy(),
-               mask=mask.numpy(), gate=gate.numpy())
+               dlogits=Z.grad.numpy(), mask=mask.numpy(), gate=gate.detach().numpy())
     return out
 
 
@@ -242,8 +246,9 @@ def _run_oracle(orc, logits, x, W1, W3, W2, dy, K, act):
     eti, off, tim = orc.build_indices(tei, E)
     y, A, B = orc.ffn_forward(x, W1, W3, W2, eti, off, tim, gates, act)
     dx, dW1, dW3, dW2 = orc.ffn_backward(dy, x, W1, W3, W2, eti, off, tim, gates, act)
+    dz = orc.router_backward(dy, x, W1, W3, W2, eti, off, tei, tim, gates, act)
     return dict(tei=tei, gates=gates, eti=eti, off=off, tim=tim, y=y, A=A, B=B,
-                dx=dx, dW1=dW1, dW3=dW3, dW2=dW2)
+                dx=dx, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dz)
 
 
 DENSE_CASES = [
@@ -265,7 +270,7 @@ def check_dense_mask(orc):
         sel = np.zeros((L, E), dtype=bool)
         np.put_along_axis(sel, o["tei"].astype(np.int64), True, axis=1)
         assert np.array_equal(sel, ref["mask"]), i
-        for name in ("y", "dx", "dW1", "dW2") + (("dW3",) if act == SWIGLU else ()):
+        for name in ("y", "dx", "dW1", "dW2", "dlogits") + (("dW3",) if act == SWIGLU else ()):
             err = relerr(o[name], ref[name])
             assert err < 1e-6, (i, name, err)
 
@@ -334,6 +339,61 @@ def check_sampled_consistency(orc):
                 assert np.allclose(c3, o["dW3"][e][:, cols], rtol=1e-12, atol=1e-13), (i, e)
 
 
+def _gates64(logits, tei):
+    """Softmax over each token's selected logits, in float64."""
+    z = np.take_along_axis(np.asarray(logits, dtype=np.float64), np.asarray(tei, dtype=np.int64), axis=1)
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def check_router_finite_differences(orc):
+    """<y, dy> as a function of the logits, with the selection held (the
+    direction is small enough not to change any token's top K)."""
+    for i, (L, d, h, E, K, act, ints) in enumerate(DENSE_CASES[:3]):
+        if ints:
+            continue
+        logits, x, W1, W3, W2, dy = tiny_inputs(L, d, h, E, K, act, 140 + i)
+        tei, _ = orc.route(logits, K)
+        eti, off, tim = orc.build_indices(tei, E)
+        z0 = np.asarray(logits, dtype=np.float64)
+
+        def loss(z):
+            y, _, _ = orc.ffn_forward(x, W1, W3, W2, eti, off, tim, _gates64(z, tei), act)
+            return float((y * dy).sum())
+
+        dz = orc.router_backward(dy, x, W1, W3, W2, eti, off, tei, tim, _gates64(z0, tei), act)
+        rng = np.random.default_rng(7 + i)
+        eps = 1e-6
+        for _ in range(3):
+            V = rng.standard_normal(z0.shape)
+            for zz in (z0 + eps * V, z0 - eps * V):
+                t2, _ = orc.route(zz.astype(np.float32), K)
+                assert np.array_equal(t2, tei), "direction changed the selection"
+            fd = (loss(z0 + eps * V) - loss(z0 - eps * V)) / (2 * eps)
+            an = float((dz * V).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (i, fd, an)
+
+
+def check_router_special_cases(orc):
+    # K = 1: every gate is exactly 1, so the logits get no gradient
+    logits, x, W1, W3, W2, dy = tiny_inputs(21, 4, 6, 5, 1, SWIGLU, 31)
+    o = _run_oracle(orc, logits, x, W1, W3, W2, dy, 1, SWIGLU)
+    assert np.all(o["dlogits"] == 0)
+    # unselected logits get exactly 0; each row of a softmax Jacobian sums to 0
+    logits, x, W1, W3, W2, dy = tiny_inputs(25, 5, 4, 6, 3, SILU, 32)
+    o = _run_oracle(orc, logits, x, W1, W3, W2, dy, 3, SILU)
+    sel = np.zeros(logits.shape, dtype=bool)
+    np.put_along_axis(sel, o["tei"].astype(np.int64), True, axis=1)
+    assert np.all(o["dlogits"][~sel] == 0)
+    g64 = _gates64(logits, o["tei"])
+    dz = orc.router_backward(dy, x, W1, W3, W2, o["eti"], o["off"], o["tei"], o["tim"], g64, SILU)
+    assert np.abs(dz.sum(axis=1)).max() <= 1e-12 * max(1.0, np.abs(dz).max())
+    # sampled rows agree with the full gradient
+    toks = np.array([0, 12, 24])
+    rows = orc.router_rows(toks, dy, x, W1, W3, W2, o["tei"], o["gates"], SILU, 6)
+    assert relerr(rows, o["dlogits"][toks]) < 1e-12
+
+
 def check_empty_expert(orc):
     logits, x, W1, W3, W2, dy = tiny_inputs(20, 4, 4, 4, 2, SWIGLU, 77)
     logits[:, 2] = -1e4                    # expert 2 never chosen
@@ -358,6 +418,8 @@ ALL_CHECKS = [
     check_dense_mask,
     check_textbook_mlp,
     check_finite_differences,
+    check_router_finite_differences,
+    check_router_special_cases,
     check_sampled_consistency,
     check_empty_expert,
     check_checkpoint_size,

@@ -59,6 +59,15 @@ MUTATIONS = [
     ("sampled dW2 rows without gate",
      "dO = g[:, None] * np.asarray(dy[toks], dtype=np.float64)",
      "dO = np.asarray(dy[toks], dtype=np.float64)"),
+    ("router gradient without the softmax mean term",
+     "    return gates * (dgate - s)",
+     "    return gates * dgate"),
+    ("router gradient from the gated output",
+     "        dgate[:, k] = (dy * O[tim[:, k]]).sum(axis=1)",
+     "        dgate[:, k] = (dy * gates[:, k:k + 1] * O[tim[:, k]]).sum(axis=1)"),
+    ("router gradient in slot order instead of expert columns",
+     "    np.put_along_axis(dz, np.asarray(tei, dtype=np.int64), _softmax_backward(gates, dgate), axis=1)",
+     "    dz[:, :K] = _softmax_backward(gates, dgate)"),
 ]
 
 
