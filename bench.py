@@ -6,7 +6,9 @@ batch of synthetic inputs already resident in HBM.  Prints one JSON line:
 routed tokens/s (L per step time), per-kernel times from HIP events recorded
 by the library on the launch stream, the roofline of the dominant kernel,
 the dispatch builder's HBM roofline, and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload.  The router-logit gradient (optional output of
+the backward) is not part of the step; it is timed separately afterwards
+(`router_grad`: its kernel and the extra time of the dG kernel that feeds it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
 """
@@ -152,6 +154,40 @@ def measured_traffic(kernel, workload):
     if not ent or ent.get("source_hash") != source_hash():
         return None
     return ent.get("bytes_per_launch")
+
+
+def router_grad_bytes(cfg):
+    """Algorithmic HBM bytes of the router-logit gradient: the dG kernel's
+    per-route partials written and read (4 R ceil(h/256)), token_index_map,
+    token_expert_indices and gates read (12 L K), dlogits written (4 L E)."""
+    nN = -(-cfg.h // 256)
+    return 2 * 4 * cfg.R * nN + 12 * cfg.L * cfg.K + 4 * cfg.L * cfg.E
+
+
+def time_router_grad(cfg, buf, inp, per_kernel, reps=2):
+    """forward + backward with dlogits requested, `reps` times, timed per kernel."""
+    buf.dlogits = torch.empty(cfg.L, cfg.E, dtype=torch.float32, device=buf.device)
+    torch.cuda.synchronize()
+    B.profile_reset()
+    B.profile_enable(True)
+    for _ in range(reps):
+        buf.forward(inp["x"], inp["W1"], inp["W3"], inp["W2"])
+        buf.backward(inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"])
+    torch.cuda.synchronize()
+    B.profile_enable(False)
+    st = B.profile_read()
+    buf.dlogits = None
+    kn, kms = st.get("router_grad", (0, 0.0))
+    b1n, b1ms = st.get("ffn_b1_dgrad_glu", (0, 0.0))
+    k_ms = kms / max(kn, 1)
+    b1_with = b1ms / max(b1n, 1)
+    b1_without = per_kernel.get("ffn_b1_dgrad_glu", {}).get("avg_launch_ms", 0.0)
+    nbytes = router_grad_bytes(cfg)
+    return {"kernel_ms": k_ms, "dgrad_kernel_ms_with": b1_with,
+            "dgrad_kernel_ms_without": b1_without,
+            "extra_ms_per_step": k_ms + b1_with - b1_without,
+            "bytes": nbytes,
+            "kernel_gbs": (nbytes - 4 * cfg.R * -(-cfg.h // 256)) / (k_ms / 1e3) / 1e9 if k_ms > 0 else None}
 
 
 def cpu_baseline(cfg, inp, budget_s=15.0):
@@ -301,6 +337,7 @@ def main():
         "gemm_tflops_all": total_flops / (gemm_ms / 1e3) / 1e12,
         "kernels": per_kernel,
     }
+    out["router_grad"] = time_router_grad(cfg, buf, inp, per_kernel)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, inp)

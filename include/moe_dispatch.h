@@ -146,14 +146,23 @@ int moe_ffn_forward(const moe_shape* s, const void* x, const void* W1, const voi
  *      A, B: the checkpoint written by moe_ffn_forward for the same inputs.
  * Out: dx [L, d]; dW1, dW3 [E, d, h]; dW2 [E, h, d].  dW outputs are
  *      overwritten (not accumulated); an expert with no routes gets exact 0.
+ *      dlogits [L, E] float32, optional (NULL: not computed): the gradient
+ *      with respect to the router logits.  The pages do not describe it; it
+ *      is the derivative of the same forward with the gates a softmax over
+ *      the K selected logits:
+ *        dg[t,k] = <dy[t], O[p(t,k)]>  (O = the route's un-gated output G W2_e),
+ *        dlogits[t, e_k] = gates[t,k] * (dg[t,k] - sum_j gates[t,j] dg[t,j]),
+ *      0 for the experts a token did not select (the selection is piecewise
+ *      constant).  dg is formed in float32 from the recomputed G and
+ *      dy W2_e^T, summed over 256-column tiles in a fixed order.
  * Clobbers A and B (they hold dA and dB on return).
  */
 int moe_ffn_backward(const moe_shape* s, const void* dy, const void* x, const void* W1,
                      const void* W3, const void* W2, const int32_t* expert_token_indices,
                      const int32_t* expert_token_offsets, const int32_t* token_expert_indices,
                      const int32_t* token_index_map, const float* gates, void* A, void* B,
-                     void* dx, void* dW1, void* dW3, void* dW2, void* ws, size_t* ws_bytes,
-                     void* stream);
+                     void* dx, void* dW1, void* dW3, void* dW2, float* dlogits, void* ws,
+                     size_t* ws_bytes, void* stream);
 
 /* Text describing the last non-OK return on the calling thread ("" if none).
  * The pointer stays valid until the next call on the same thread. */

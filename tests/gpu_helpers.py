@@ -81,7 +81,7 @@ def full_inputs_host(inp):
 def run_full_parity(cfg, seed, device, inp=None, check_determinism=False):
     """Whole-tensor parity for shapes the oracle runs in seconds."""
     inp = inp or W.make_inputs(cfg, seed, device)
-    buf = MoELayerBuffers(cfg, device)
+    buf = MoELayerBuffers(cfg, device, router_grad=True)
     h_in = full_inputs_host(inp)
     ref = oracle_dispatch(h_in["logits"], cfg)
     buf.build(inp["logits"])
@@ -102,6 +102,10 @@ def run_full_parity(cfg, seed, device, inp=None, check_determinism=False):
         assert_close("B", B_gpu, B, tol)
     assert_close("y", y_gpu, y, tol)
     assert_close("dx", host(buf.dx), dx, tol)
+    dz = oracle.router_backward(h_in["dy"], h_in["x"], h_in["W1"], h_in["W3"], h_in["W2"],
+                                ref["eti"], ref["off"], ref["tei"], ref["tim"], ref["gates"],
+                                cfg.act)
+    assert_close("dlogits", host(buf.dlogits), dz, tol)
     gW1, gW2 = host(buf.dW1), host(buf.dW2)
     gW3 = host(buf.dW3)
     for e in range(cfg.E):
@@ -127,7 +131,7 @@ def run_sampled_parity(cfg, seed, device, n_tokens=48, n_experts=2, n_cols=4):
     of dW1/dW3 (and rows of dW2) for sampled experts."""
     say(f"  sampled parity {cfg.name} seed {seed}")
     inp = W.make_inputs(cfg, seed, device)
-    buf = MoELayerBuffers(cfg, device)
+    buf = MoELayerBuffers(cfg, device, router_grad=True)
     logits = inp["logits"].cpu().numpy()
     ref = oracle_dispatch(logits, cfg)
     buf.build(inp["logits"])
@@ -143,6 +147,7 @@ def run_sampled_parity(cfg, seed, device, n_tokens=48, n_experts=2, n_cols=4):
     buf.backward(inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"])
     torch.cuda.synchronize()
     dx_s = _rows(buf.dx, toks)
+    dz_s = _rows(buf.dlogits, toks)
     tol = tol_of(cfg)
 
     W1h, W2h = host(inp["W1"]), host(inp["W2"])
@@ -161,6 +166,9 @@ def run_sampled_parity(cfg, seed, device, n_tokens=48, n_experts=2, n_cols=4):
         assert_close("B rows", B_s, B_r, tol)
     assert_close("y rows", y_s, y_r, tol)
     assert_close("dx rows", dx_s, dx_r, tol)
+    dz_r = oracle.router_rows(np.arange(toks.size), dys, xs, W1h, W3h, W2h, ref["tei"][toks],
+                              ref["gates"][toks], cfg.act, cfg.E)
+    assert_close("dlogits rows", dz_s, dz_r, tol)
 
     counts = np.diff(off)
     nonempty = np.flatnonzero(counts > 0)

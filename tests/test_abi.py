@@ -67,6 +67,8 @@ def call_fwd(lib, shape, ptrs=None, ws=FAKE, nbytes=0):
 
 def call_bwd(lib, shape, ptrs=None, ws=FAKE, nbytes=0):
     p = ptrs or [FAKE] * 16
+    if len(p) == 16:
+        p = p + [None]           # dlogits: optional
     n = ctypes.c_size_t(nbytes)
     rc = lib.moe_ffn_backward(ctypes.byref(shape), *p, ws, ctypes.byref(n), None)
     return rc, n.value
@@ -153,6 +155,13 @@ def test_backward_null_pointer(lib, i):
     assert call_bwd(lib, shp(), p)[0] == B.MOE_ERR_INVALID_ARG
     if i in (3, 11, 14):          # W3, B, dW3 unused for SiLU
         assert call_bwd(lib, shp(act=B.MOE_SILU), p, ws=None)[0] == B.MOE_OK
+
+
+def test_backward_optional_router_gradient(lib):
+    # dlogits may be NULL or any 4-byte aligned address; 2-byte aligned is rejected
+    assert call_bwd(lib, shp(), [FAKE] * 16 + [None])[0] == B.MOE_ERR_WORKSPACE
+    assert call_bwd(lib, shp(), [FAKE] * 16 + [FAKE + 4])[0] == B.MOE_ERR_WORKSPACE
+    assert call_bwd(lib, shp(), [FAKE] * 16 + [FAKE + 2])[0] == B.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_query_and_too_small(lib):

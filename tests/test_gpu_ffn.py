@@ -85,7 +85,7 @@ def test_bitwise_repeatable_and_poisoned_workspace():
     inp = W.make_inputs(cfg, 21, dev)
     outs = []
     for poison in (None, 0xFF, 0x00):
-        buf = MoELayerBuffers(cfg, dev)
+        buf = MoELayerBuffers(cfg, dev, router_grad=True)
         if poison is not None:
             buf.ws.fill_(poison)
         buf.build(inp["logits"])
@@ -93,7 +93,8 @@ def test_bitwise_repeatable_and_poisoned_workspace():
         AB = (buf.A.clone(), buf.B.clone(), buf.y.clone())
         buf.backward(inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"])
         torch.cuda.synchronize()
-        outs.append(AB + (buf.dx.clone(), buf.dW1.clone(), buf.dW3.clone(), buf.dW2.clone()))
+        outs.append(AB + (buf.dx.clone(), buf.dW1.clone(), buf.dW3.clone(), buf.dW2.clone(),
+                          buf.dlogits.clone()))
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
@@ -101,20 +102,22 @@ def test_bitwise_repeatable_and_poisoned_workspace():
 
 
 def test_outputs_leave_neighbours_untouched():
-    """Guard bands around y and dx stay untouched (no write outside the
-    outputs)."""
+    """Guard bands around y, dx and dlogits stay untouched (no write outside
+    the outputs)."""
     dev = require_gpu()
     cfg = W.small_config(999, 128, 256, 8, 2, SWIGLU, W.BF16)
     inp = W.make_inputs(cfg, 8, dev)
-    buf = MoELayerBuffers(cfg, dev)
+    buf = MoELayerBuffers(cfg, dev, router_grad=True)
     pad = 4096
     ystore = torch.full((cfg.L * cfg.d + 2 * pad,), 7.0, dtype=torch.bfloat16, device=dev)
     dxstore = torch.full((cfg.L * cfg.d + 2 * pad,), 7.0, dtype=torch.bfloat16, device=dev)
     buf.y = ystore[pad:pad + cfg.L * cfg.d].view(cfg.L, cfg.d)
     buf.dx = dxstore[pad:pad + cfg.L * cfg.d].view(cfg.L, cfg.d)
+    dzstore = torch.full((cfg.L * cfg.E + 2 * pad,), 7.0, dtype=torch.float32, device=dev)
+    buf.dlogits = dzstore[pad:pad + cfg.L * cfg.E].view(cfg.L, cfg.E)
     buf.build(inp["logits"])
     buf.forward(inp["x"], inp["W1"], inp["W3"], inp["W2"])
     buf.backward(inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"])
     torch.cuda.synchronize()
-    for s in (ystore, dxstore):
+    for s in (ystore, dxstore, dzstore):
         assert torch.all(s[:pad] == 7.0) and torch.all(s[-pad:] == 7.0)

@@ -71,7 +71,8 @@ def load_library(path: str = LIB_PATH):
     S = ctypes.POINTER(Shape)
     lib.moe_dispatch_build.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
     lib.moe_ffn_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
-    lib.moe_ffn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_ffn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ,
+                                     P]
     for f in ("moe_dispatch_build", "moe_ffn_forward", "moe_ffn_backward",
               "moe_profile_enable", "moe_profile_reset", "moe_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
@@ -132,8 +133,9 @@ def workspace_bytes(name: str, shape: Shape) -> int:
     lib = load_library()
     fn = getattr(lib, name)
     n = {"moe_dispatch_build": 6, "moe_ffn_forward": 12, "moe_ffn_backward": 16}[name]
+    tail = [None] if name == "moe_ffn_backward" else []   # dlogits: optional, not needed
     nbytes = ctypes.c_size_t(0)
-    _check(fn(ctypes.byref(shape), *([256] * n), None, ctypes.byref(nbytes), None))
+    _check(fn(ctypes.byref(shape), *([256] * n), *tail, None, ctypes.byref(nbytes), None))
     return int(nbytes.value)
 
 
@@ -152,11 +154,12 @@ def moe_ffn_forward(shape, x, W1, W3, W2, eti, offsets, tei, tim, gates, y, A, B
 
 
 def moe_ffn_backward(shape, dy, x, W1, W3, W2, eti, offsets, tei, tim, gates, A, B,
-                     dx, dW1, dW3, dW2, ws=None, stream=None):
+                     dx, dW1, dW3, dW2, dlogits=None, ws=None, stream=None):
+    """dlogits: optional [L, E] float32 output, the router-logit gradient."""
     lib = load_library()
     args = [_ptr(dy), _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(eti), _ptr(offsets),
             _ptr(tei), _ptr(tim), _ptr(gates), _ptr(A), _ptr(B), _ptr(dx), _ptr(dW1),
-            _ptr(dW3), _ptr(dW2)]
+            _ptr(dW3), _ptr(dW2), _ptr(dlogits)]
     return _run(lib.moe_ffn_backward, shape, args, ws, stream, x.device)
 
 

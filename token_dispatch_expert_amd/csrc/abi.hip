@@ -220,8 +220,8 @@ int moe_ffn_forward(const moe_shape* s, const void* x, const void* W1, const voi
 int moe_ffn_backward(const moe_shape* s, const void* dy, const void* x, const void* W1,
                      const void* W3, const void* W2, const int32_t* eti, const int32_t* offsets,
                      const int32_t* tei, const int32_t* tim, const float* gates, void* A, void* B,
-                     void* dx, void* dW1, void* dW3, void* dW2, void* ws, size_t* ws_bytes,
-                     void* stream) {
+                     void* dx, void* dW1, void* dW3, void* dW2, float* dlogits, void* ws,
+                     size_t* ws_bytes, void* stream) {
   g_err.clear();
   int rc = check_ffn_shape(s);
   if (rc != MOE_OK) return rc;
@@ -238,14 +238,17 @@ int moe_ffn_backward(const moe_shape* s, const void* dy, const void* x, const vo
     rc = check_ptrs(pg, 3);
     if (rc != MOE_OK) return rc;
   }
+  if (dlogits != nullptr && !aligned(dlogits, 4))
+    return fail(MOE_ERR_INVALID_ARG, "dlogits must be 4-byte aligned");
   const moe::FfnDims dm = dims_of(s);
   const moe::FfnPlan pl = moe::plan_ffn(dm, true);
   bool query = false;
   rc = check_ws(ws, ws_bytes, pl.bytes, &query);
   if (rc != MOE_OK || query) return rc;
   hipError_t e = moe::launch_backward(pl, dm, dy, x, W1, glu ? W3 : W1, W2, eti, offsets, tim,
-                                      gates, A, glu ? B : A, dx, dW1, glu ? dW3 : dW1, dW2,
-                                      static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+                                      gates, A, glu ? B : A, dx, dW1, glu ? dW3 : dW1, dW2, tei,
+                                      dlogits, static_cast<char*>(ws),
+                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "moe_ffn_backward launch");
   return MOE_OK;
 }

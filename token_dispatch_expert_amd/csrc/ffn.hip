@@ -827,14 +827,19 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
 }
 
 // B1: dG = gate * (dy[t] W2_e^T) per route; epilogue recomputes SiLU from
-// the checkpoint and writes dA, dB over A, B and Gs = gate * G.
-template <typename T, bool DUAL>
+// the checkpoint and writes dA, dB over A, B and Gs = gate * G.  ROUTER: it
+// also leaves, for every route row p, the tile's share of the router
+// gradient's <dy[t] W2_e^T, G[p]> (= <dy[t], O[p]>, O the route's un-gated
+// output) in dgp[p * nN + ntile]: each thread's products are summed over its
+// columns, parked in LDS, and added per row in a fixed order.
+template <typename T, bool DUAL, bool ROUTER>
 __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __restrict__ dy,
                                                       const T* __restrict__ W2,
                                                       const int32_t* __restrict__ eti,
                                                       const float* __restrict__ gate_p, int d,
                                                       int h, T* __restrict__ A,
-                                                      T* __restrict__ B, T* __restrict__ Gs) {
+                                                      T* __restrict__ B, T* __restrict__ Gs,
+                                                      float* __restrict__ dgp) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
@@ -860,48 +865,114 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
   __syncthreads();
 
+  // LDS after the main loop (ROUTER): [256 rows][128 column lanes] of
+  // row-dot products
+  float* s_part = reinterpret_cast<float*>(smem);
+  const int pcol = wave_n() * 32 + ((threadIdx.x & 63) & 31);
+  constexpr int IB = 16;  // rows of checkpoint loads in flight
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    float av[16][NTL], bv[16][NTL];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = rb + acc_row(mt, i);
+    for (int i0 = 0; i0 < 16; i0 += IB) {
+      float av[IB][NTL], bv[IB][NTL];
 #pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) {
-        const int c = n0 + acc_col(nt);
-        const bool ok = p < re && c < h;
-        const int64_t o = ok ? (int64_t)p * h + c : 0;
-        av[i][nt] = Elem<T>::load(A + o);
-        bv[i][nt] = DUAL ? Elem<T>::load(B + o) : 0.f;
-      }
-    }
+      for (int ii = 0; ii < IB; ++ii) {
+        const int p = rb + acc_row(mt, i0 + ii);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = acc_row(mt, i);
-      const int p = rb + row;
-      const float gp = s_g[row];
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) {
-        const int c = n0 + acc_col(nt);
-        if (p >= re || c >= h) continue;
-        const int64_t o = (int64_t)p * h + c;
-        const float dg = gp * acc.c[mt][nt][i];
-        const float a = av[i][nt];
-        const float s = sigm_of<T>(a);
-        const float sl = a * s;
-        const float ds_ = s * (1.0f + a * (1.0f - s));
-        if (DUAL) {
-          const float b = bv[i][nt];
-          Elem<T>::store(A + o, dg * b * ds_);
-          Elem<T>::store(B + o, dg * sl);
-          Elem<T>::store(Gs + o, gp * sl * b);
-        } else {
-          Elem<T>::store(A + o, dg * ds_);
-          Elem<T>::store(Gs + o, gp * sl);
+        for (int nt = 0; nt < NTL; ++nt) {
+          const int c = n0 + acc_col(nt);
+          const bool ok = p < re && c < h;
+          const int64_t o = ok ? (int64_t)p * h + c : 0;
+          av[ii][nt] = Elem<T>::load(A + o);
+          bv[ii][nt] = DUAL ? Elem<T>::load(B + o) : 0.f;
         }
+      }
+#pragma unroll
+      for (int ii = 0; ii < IB; ++ii) {
+        const int i = i0 + ii;
+        const int row = acc_row(mt, i);
+        const int p = rb + row;
+        const float gp = s_g[row];
+        float rdot = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+          const int c = n0 + acc_col(nt);
+          if (p >= re || c >= h) continue;
+          const int64_t o = (int64_t)p * h + c;
+          const float dg = gp * acc.c[mt][nt][i];
+          const float a = av[ii][nt];
+          const float s = sigm_of<T>(a);
+          const float sl = a * s;
+          const float ds_ = s * (1.0f + a * (1.0f - s));
+          if (DUAL) {
+            const float b = bv[ii][nt];
+            Elem<T>::store(A + o, dg * b * ds_);
+            Elem<T>::store(B + o, dg * sl);
+            Elem<T>::store(Gs + o, gp * sl * b);
+            if (ROUTER) rdot += acc.c[mt][nt][i] * (sl * b);
+          } else {
+            Elem<T>::store(A + o, dg * ds_);
+            Elem<T>::store(Gs + o, gp * sl);
+            if (ROUTER) rdot += acc.c[mt][nt][i] * sl;
+          }
+        }
+        if (ROUTER) s_part[row * 128 + pcol] = rdot;
       }
     }
   }
+  if (ROUTER) {
+    __syncthreads();
+    // each row is read by two adjacent lanes (one half each), starting at a
+    // lane-dependent column so that a wavefront's reads hit 64 distinct banks;
+    // a given row is always summed by the same lane in the same order
+    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int rot = (row + 32 * half) & 63;
+    float v = 0.f;
+    for (int j = 0; j < 64; ++j) v += s_part[row * 128 + half * 64 + ((j + rot) & 63)];
+    const float other = __shfl_xor(v, 1);
+    const float tot = half == 0 ? v + other : other + v;  // same order in both lanes
+    const int p = rb + row;
+    if (half == 0 && p < re) dgp[(int64_t)p * ra.nN + ntile] = tot;
+  }
+}
+
+// Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
+// its token's route partials into dg_k = <dy[t], O[tim[t, k]]> (partials in
+// ascending tile order), forms the softmax backward over the selected logits
+// dz_k = g_k (dg_k - sum_j g_j dg_j) and parks the row in LDS; then the
+// workgroup writes the 64 full rows of dlogits (zeros for experts not chosen).
+__global__ __launch_bounds__(256) void router_grad(const int32_t* __restrict__ tei,
+                                                   const int32_t* __restrict__ tim,
+                                                   const float* __restrict__ gates,
+                                                   const float* __restrict__ dgp, int nN,
+                                                   int64_t L, int E, int K,
+                                                   float* __restrict__ dz) {
+  __shared__ float s_rows[64 * 256];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int nrow = (int)min<int64_t>(64, L - t0);
+  for (int i = threadIdx.x; i < nrow * E; i += 256) s_rows[i] = 0.f;
+  __syncthreads();
+  if (threadIdx.x < nrow) {
+    const int64_t t = t0 + threadIdx.x;
+    const int32_t* tm = tim + t * K;
+    const float* g = gates + t * K;
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const float* q = dgp + (int64_t)tm[k] * nN;
+      float dg = 0.f;
+      for (int j = 0; j < nN; ++j) dg += q[j];
+      sum += g[k] * dg;
+    }
+    for (int k = 0; k < K; ++k) {
+      const float* q = dgp + (int64_t)tm[k] * nN;
+      float dg = 0.f;
+      for (int j = 0; j < nN; ++j) dg += q[j];
+      s_rows[threadIdx.x * E + tei[t * K + k]] = g[k] * (dg - sum);
+    }
+  }
+  __syncthreads();
+  float* out = dz + t0 * E;
+  for (int i = threadIdx.x; i < nrow * E; i += 256) out[i] = s_rows[i];
 }
 
 struct WeightArgs {           // weight-gradient tiles: E x nM x nN
@@ -1092,6 +1163,8 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   p.off_base = o;   o = align_up(o + (size_t)dm.K * p.list_chunks * 4, 256);
   p.off_peoff = o;  o = align_up(o + (size_t)dm.K * (dm.E + 1) * 4, 256);
   p.off_gatep = o;  o = align_up(o + (backward ? (size_t)p.R * 4 : 0), 256);
+  // router gradient: per route, one partial <dG row, G row> per 256-column tile
+  p.off_dgp = o;    o = align_up(o + (backward ? (size_t)p.R * cdiv(dm.h, 256) * 4 : 0), 256);
   p.off_tiles_route = o; o = align_up(o + (size_t)p.route_tiles * 16, 256);
   p.off_tiles_pass = o;  o = align_up(o + (size_t)dm.K * p.pass_tiles * 16, 256);
   const int nW = backward ? 0 : (dm.act == 1 ? 3 : 2);   // W1T, W2T, (W3T)
@@ -1202,23 +1275,35 @@ template <typename T>
 static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const T* x, const T* W1,
                        const T* W3, const T* W2, const int32_t* eti, const int32_t* offsets,
                        const int32_t* tim, const float* gates, T* A, T* B, T* dx, T* dW1, T* dW3,
-                       T* dW2, char* ws, hipStream_t s) {
+                       T* dW2, const int32_t* tei, float* dlogits, char* ws, hipStream_t s) {
   const bool f32 = sizeof(T) == 4;
   const bool dual = dm.act == 1;
   float* gate_p = reinterpret_cast<float*>(ws + pl.off_gatep);
   Lists ls = build_lists(pl, dm, offsets, tim, gates, gate_p, ws, s);
   T* Gs = reinterpret_cast<T*>(ws + pl.off_g);
   float* acc = f32 ? reinterpret_cast<float*>(dx) : reinterpret_cast<float*>(ws + pl.off_acc);
+  float* dgp = dlogits != nullptr ? reinterpret_cast<float*>(ws + pl.off_dgp) : nullptr;
+  const int nNh = (int)cdiv(dm.h, 256);
   {
     LaunchTimer lt("ffn_b1_dgrad_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, 256), (const char*)ls.zero};
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, nNh, (const char*)ls.zero};
     const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
-    if (dual)
-      hipLaunchKernelGGL((b1_dgrad_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti,
-                         gate_p, dm.d, dm.h, A, B, Gs);
-    else
-      hipLaunchKernelGGL((b1_dgrad_glu<T, false>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti,
-                         gate_p, dm.d, dm.h, A, B, Gs);
+#define MOE_B1(DU, RO)                                                                          \
+  hipLaunchKernelGGL((b1_dgrad_glu<T, DU, RO>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti, gate_p, \
+                     dm.d, dm.h, A, B, Gs, dgp)
+    if (dual) {
+      if (dgp != nullptr) MOE_B1(true, true);
+      else MOE_B1(true, false);
+    } else {
+      if (dgp != nullptr) MOE_B1(false, true);
+      else MOE_B1(false, false);
+    }
+#undef MOE_B1
+  }
+  if (dlogits != nullptr) {
+    LaunchTimer lt("router_grad", s);
+    hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, 64)), dim3(256), 0, s, tei, tim,
+                       gates, dgp, nNh, dm.L, dm.E, dm.K, dlogits);
   }
   {
     LaunchTimer lt("ffn_b0_dw2", s);
@@ -1270,16 +1355,17 @@ hipError_t launch_backward(const FfnPlan& pl, const FfnDims& dm, const void* dy,
                            const void* W1, const void* W3, const void* W2, const int32_t* eti,
                            const int32_t* offsets, const int32_t* tim, const float* gates,
                            void* A, void* B, void* dx, void* dW1, void* dW3, void* dW2,
-                           char* ws, hipStream_t s) {
+                           const int32_t* tei, float* dlogits, char* ws, hipStream_t s) {
   if (dm.dtype == 1)
     backward_t<bf16_t>(pl, dm, (const bf16_t*)dy, (const bf16_t*)x, (const bf16_t*)W1,
                        (const bf16_t*)W3, (const bf16_t*)W2, eti, offsets, tim, gates,
                        (bf16_t*)A, (bf16_t*)B, (bf16_t*)dx, (bf16_t*)dW1, (bf16_t*)dW3,
-                       (bf16_t*)dW2, ws, s);
+                       (bf16_t*)dW2, tei, dlogits, ws, s);
   else
     backward_t<float>(pl, dm, (const float*)dy, (const float*)x, (const float*)W1,
                       (const float*)W3, (const float*)W2, eti, offsets, tim, gates, (float*)A,
-                      (float*)B, (float*)dx, (float*)dW1, (float*)dW3, (float*)dW2, ws, s);
+                      (float*)B, (float*)dx, (float*)dW1, (float*)dW3, (float*)dW2, tei, dlogits,
+                      ws, s);
   return hipGetLastError();
 }
 

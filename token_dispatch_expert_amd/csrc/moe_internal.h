@@ -47,7 +47,7 @@ struct FfnPlan {
   int64_t route_tiles;   // upper bound of route-major M tiles
   int64_t pass_tiles;    // upper bound of M tiles per slot pass
   int64_t list_chunks;   // chunks of the slot-list builder
-  size_t off_g, off_acc, off_slot, off_list, off_cnt, off_base, off_peoff, off_gatep;
+  size_t off_g, off_acc, off_slot, off_list, off_cnt, off_base, off_peoff, off_gatep, off_dgp;
   size_t off_tiles_route, off_tiles_pass, off_wt, off_zero, bytes;
 };
 FfnPlan plan_ffn(const FfnDims& dm, bool backward);
@@ -61,6 +61,6 @@ hipError_t launch_backward(const FfnPlan& pl, const FfnDims& dm, const void* dy,
                            const void* W1, const void* W3, const void* W2, const int32_t* eti,
                            const int32_t* offsets, const int32_t* tim, const float* gates,
                            void* A, void* B, void* dx, void* dW1, void* dW3, void* dW2,
-                           char* ws, hipStream_t s);
+                           const int32_t* tei, float* dlogits, char* ws, hipStream_t s);
 
 }  // namespace moe

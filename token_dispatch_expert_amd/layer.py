@@ -15,7 +15,10 @@ from .workloads import MoEConfig, SWIGLU, F32
 
 
 class MoELayerBuffers:
-    def __init__(self, cfg: MoEConfig, device="cuda"):
+    """router_grad=True also allocates dlogits [L, E] float32 and asks the
+    backward for the router-logit gradient."""
+
+    def __init__(self, cfg: MoEConfig, device="cuda", router_grad: bool = False):
         self.cfg = cfg
         self.device = torch.device(device)
         L, d, h, E, K = cfg.L, cfg.d, cfg.h, cfg.E, cfg.K
@@ -37,6 +40,7 @@ class MoELayerBuffers:
         self.dW1 = torch.empty(E, d, h, dtype=dt, device=dev)
         self.dW3 = torch.empty(E, d, h, dtype=dt, device=dev) if cfg.act == SWIGLU else None
         self.dW2 = torch.empty(E, h, d, dtype=dt, device=dev)
+        self.dlogits = torch.empty(L, E, dtype=torch.float32, device=dev) if router_grad else None
         nbytes = max(B.workspace_bytes("moe_dispatch_build", self.shape),
                      B.workspace_bytes("moe_ffn_forward", self.shape),
                      B.workspace_bytes("moe_ffn_backward", self.shape))
@@ -53,7 +57,7 @@ class MoELayerBuffers:
     def backward(self, dy, x, W1, W3, W2, stream=None):
         B.moe_ffn_backward(self.shape, dy, x, W1, W3, W2, self.eti, self.offsets, self.tei,
                            self.tim, self.gates, self.A, self.B, self.dx, self.dW1, self.dW3,
-                           self.dW2, ws=self.ws, stream=stream)
+                           self.dW2, dlogits=self.dlogits, ws=self.ws, stream=stream)
 
     def step(self, inp: dict, stream=None):
         """Build + forward + backward on the inputs of workloads.make_inputs."""
