@@ -11,6 +11,8 @@ the backward) is not part of the step; it is timed separately afterwards
 (`router_grad`: its kernel and the extra time of the dG kernel that feeds it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
+       python bench.py --study memory|dispatch-e|skew   (extra measurements,
+       one JSON line per point, instead of the step benchmark)
 """
 
 from __future__ import annotations
@@ -190,6 +192,96 @@ def time_router_grad(cfg, buf, inp, per_kernel, reps=2):
             "kernel_gbs": (nbytes - 4 * cfg.R * -(-cfg.h // 256)) / (k_ms / 1e3) / 1e9 if k_ms > 0 else None}
 
 
+def _emit(d):
+    print(json.dumps(d), flush=True)
+
+
+def study_memory(cfg, seed, dev):
+    """Device memory of one layer step: what the method keeps between forward
+    and backward (A, B), the transient buffers, the measured peak (torch's
+    allocator holds every buffer), and, for scale, the two (L*K, d) buffers a
+    materialising layer keeps (routed copy of x, per-route expert output)."""
+    es = 2 if cfg.dtype == W.BF16 else 4
+    torch.zeros(1, device=dev)
+    torch.cuda.synchronize(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    inp = W.make_inputs(cfg, seed, dev)
+    torch.cuda.synchronize()
+    m_inputs = torch.cuda.memory_allocated(dev)
+    buf = MoELayerBuffers(cfg, dev)
+    torch.cuda.synchronize()
+    m_buffers = torch.cuda.memory_allocated(dev)
+    buf.step(inp)
+    torch.cuda.synchronize()
+    _emit({"study": "memory", "workload": cfg.name,
+           "checkpoint_bytes": cfg.R * cfg.h * (2 if cfg.act == W.SWIGLU else 1) * es,
+           "transient_G_bytes": cfg.R * cfg.h * es,
+           "workspace_bytes": int(buf.ws.numel()),
+           "inputs_bytes": int(m_inputs),
+           "layer_buffers_bytes": int(m_buffers - m_inputs),
+           "peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
+           "materialising_layer_extra_bytes": 2 * cfg.R * cfg.d * es})
+
+
+def study_dispatch_e(cfg, seed, dev, reps=20):
+    """Dispatch build time and HBM rate over E at the workload's L and K."""
+    for E in (8, 16, 32, 64, 128, 256):
+        if E < cfg.K:
+            continue
+        c = W.MoEConfig(f"{cfg.name}-E{E}", cfg.L, cfg.d, cfg.h, E, cfg.K, cfg.act, cfg.dtype)
+        logits = W.make_logits(c, seed, dev)
+        buf = MoELayerBuffers(W.small_config(c.L, 8, 8, E, c.K), dev)
+        buf.build(logits)
+        torch.cuda.synchronize()
+        B.profile_reset()
+        B.profile_enable(True)
+        for _ in range(reps):
+            buf.build(logits)
+        torch.cuda.synchronize()
+        B.profile_enable(False)
+        st = B.profile_read()
+        ms = sum(v[1] for k, v in st.items() if k.startswith("dispatch_")) / reps
+        nb = dispatch_bytes(c)
+        _emit({"study": "dispatch-e", "L": c.L, "E": E, "K": c.K, "ms_per_build": ms,
+               "bytes_per_build": nb, "GB/s": nb / (ms / 1e3) / 1e9,
+               "map": "bit-mask" if (E <= 64 and c.K <= 8) else "byte",
+               "kernels_ms": {k: v[1] / reps for k, v in st.items()}})
+        del buf, logits
+        torch.cuda.empty_cache()
+
+
+def study_skew(cfg, seed, dev, steps=3):
+    """Layer step time over the skew of expert loads: logits N(0,1) plus
+    2 log(w_e), w_e proportional to (e+1)^-s."""
+    import math
+    c = W.MoEConfig(f"{cfg.name}-L{cfg.L // 4}", cfg.L // 4, cfg.d, cfg.h, cfg.E, cfg.K,
+                    cfg.act, cfg.dtype)
+    inp = W.make_inputs(c, seed, dev)
+    base = inp["logits"].clone()
+    buf = MoELayerBuffers(c, dev)
+    for s in (0.0, 0.6, 1.0, 1.2, 1.5):
+        w = [(r + 1) ** (-s) for r in range(c.E)]
+        tot = sum(w)
+        bias = torch.tensor([2.0 * math.log(x / tot) for x in w], dtype=torch.float32, device=dev)
+        inp["logits"] = base + bias
+        buf.step(inp)
+        torch.cuda.synchronize()
+        load = torch.diff(buf.offsets.long()).cpu()
+        B.profile_reset()
+        B.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            buf.step(inp)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        B.profile_enable(False)
+        st = B.profile_read()
+        _emit({"study": "skew", "workload": c.name, "zipf_s": s, "ms_per_step": ms,
+               "routed_tokens_per_s": c.L / (ms / 1e3),
+               "expert_load_max": int(load.max()), "expert_load_min": int(load.min()),
+               "kernels_ms": {k: v[1] / steps for k, v in st.items()}})
+
+
 def cpu_baseline(cfg, inp, budget_s=15.0):
     """The oracle, untuned, on a bounded prefix sample of the same workload."""
     import oracle
@@ -239,6 +331,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scale reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--study", choices=("memory", "dispatch-e", "skew"),
+                    help="memory: analytic and measured device memory of one step; dispatch-e: "
+                         "dispatch build time over E at fixed L and K; skew: layer step time "
+                         "over the Zipf skew of the router logits")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/traffic.json from rocprofv3 --pmc csv output directories "
                          "and exit (no GPU needed)")
@@ -267,6 +363,10 @@ def main():
     cfg = W.CONFIGS[args.config]
     seed = args.config if args.seed is None else args.seed
     dev = torch.device("cuda:0")
+    if args.study:
+        {"memory": study_memory, "dispatch-e": study_dispatch_e, "skew": study_skew}[args.study](
+            cfg, seed, dev)
+        return
     log(f"[bench] {cfg.name}: generating inputs on {torch.cuda.get_device_name(0)}")
     inp = W.make_inputs(cfg, seed, dev)
     buf = MoELayerBuffers(cfg, dev)
