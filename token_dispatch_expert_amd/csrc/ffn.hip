@@ -980,8 +980,13 @@ struct WeightArgs {           // weight-gradient tiles: E x nM x nN
   const char* zero;           // 16 zero bytes (workspace)
 };
 
+// Weight-gradient tiles are taken in launch order, which deals the tiles of
+// one expert round-robin over the XCDs: a tile's cost is its expert's route
+// count, so giving each XCD a contiguous run of experts (as the route-major
+// products do) would pile the heaviest experts onto one XCD when loads are
+// skewed.
 __device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& mi, int& ni) {
-  const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t lid = blockIdx.x;
   const int64_t per_e = (int64_t)wa.nM * wa.nN;
   if (lid >= (int64_t)wa.E * per_e) return false;
   e = (int)(lid / per_e);
