@@ -59,6 +59,12 @@ EDGE = [
     (2500, 28, 7, "normal"),        # streaming router, 7 chunks per row
     (3000, 40, 8, "normal"),        # 64-bit expert mask with E < 64
     (3001, 64, 8, "ties"),          # largest streaming E and K
+    (1500, 128, 8, "ties"),         # lane-pair router (E <= 128), ties at the K-th value
+    (2000, 200, 5, "normal"),       # lane-quad router, last lane partly empty
+    (1200, 130, 3, "normal"),       # lane-quad router, E not a multiple of 4
+    (1100, 256, 1, "ties"),         # largest E, K = 1, ties
+    (900, 96, 8, "signed_zero"),    # lane-pair router, signed zeros
+    (3000, 252, 6, "misaligned"),   # lane-quad router, logits not 16-byte aligned
 ]
 
 

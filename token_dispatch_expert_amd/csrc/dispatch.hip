@@ -165,6 +165,166 @@ __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ lo
   }
 }
 
+// Step 1 for 64 < E <= 256 and K <= 8 (byte map): P lanes per token (P = 2
+// for E <= 128, 4 otherwise), lane q of a token holding the logits of
+// experts 64q .. 64q+63 in registers.  Each lane keeps its slice's KM
+// largest values with the med3 network; the P lists are merged across the
+// token's lanes (the partner's list is inserted into one's own, butterfly
+// order), giving the token's K-th value thr.  Each lane then marks its
+// experts with logit >= thr; surplus marks can only be ties with thr and are
+// dropped from the highest expert ids (highest lane first), and a shortfall
+// (NaN logits, outside the contract) is filled with the lowest unmarked ids,
+// so every token gets exactly K valid experts.  Slots follow the lanes'
+// order, hence ascending expert id.
+template <int P, int KM, bool VEC>
+__global__ __launch_bounds__(256) void k1_route_wide(const float* __restrict__ logits, int64_t L,
+                                                     int E, int K, int T, int C, int64_t Lpad,
+                                                     int32_t* __restrict__ tei,
+                                                     float* __restrict__ gates,
+                                                     uint8_t* __restrict__ map,
+                                                     int32_t* __restrict__ tilecnt) {
+  extern __shared__ uint4 smap_v[];
+  uint8_t* smap = reinterpret_cast<uint8_t*>(smap_v);
+  const int tile = blockIdx.x;
+  const int64_t t0 = (int64_t)tile * T;
+  const int nvec = (E * T) >> 4;
+  for (int i = threadIdx.x; i < nvec; i += 256) smap_v[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  const int q = threadIdx.x % P;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane - q;              // first lane of this token's group
+  const int e0 = 64 * q;
+  constexpr int TPP = 256 / P;           // tokens per pass (T is a multiple)
+  const uint64_t valid = E - e0 >= 64 ? ~0ull : (E > e0 ? (1ull << (E - e0)) - 1 : 0ull);
+  for (int tl = threadIdx.x / P; tl < T; tl += TPP) {
+    const int64_t t = t0 + tl;
+    const bool live = t < L;
+    const float* row = logits + (live ? t : 0) * E;
+    float v[64];
+#pragma unroll
+    for (int j4 = 0; j4 < 16; ++j4) {
+      const int e = e0 + 4 * j4;
+      if (VEC) {
+        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (live && e < E) x = *reinterpret_cast<const float4*>(row + e);  // E % 4 == 0
+        v[4 * j4] = x.x; v[4 * j4 + 1] = x.y; v[4 * j4 + 2] = x.z; v[4 * j4 + 3] = x.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[4 * j4 + u] = (live && e + u < E) ? row[e + u] : -INFINITY;
+      }
+    }
+    float b[KM];
+#pragma unroll
+    for (int i = 0; i < KM; ++i) b[i] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+#pragma unroll
+      for (int i = KM - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], v[j]);
+      b[0] = fmaxf(b[0], v[j]);
+    }
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) {
+      float pb[KM];
+#pragma unroll
+      for (int i = 0; i < KM; ++i) pb[i] = __shfl_xor(b[i], o);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+#pragma unroll
+        for (int i = KM - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], pb[j]);
+        b[0] = fmaxf(b[0], pb[j]);
+      }
+    }
+    float thr = b[0];
+#pragma unroll
+    for (int i = 1; i < KM; ++i) thr = (i == K - 1) ? b[i] : thr;
+
+    uint64_t ge = 0, gt = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      ge |= (uint64_t)(v[j] >= thr ? 1u : 0u) << j;
+      gt |= (uint64_t)(v[j] > thr ? 1u : 0u) << j;
+    }
+    ge &= valid;
+    gt &= valid;
+    // per-lane counts of the token's group, lane order = expert order
+    int cnt[P], tie[P];
+    const int mycnt = __builtin_popcountll(ge), mytie = __builtin_popcountll(ge & ~gt);
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      cnt[r] = __shfl(mycnt, grp + r);
+      tie[r] = __shfl(mytie, grp + r);
+    }
+    int total = 0, above = 0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      total += cnt[r];
+      above += r > q ? tie[r] : 0;
+    }
+    if (total > K) {  // drop surplus ties from the highest ids
+      int drop = min(max(total - K - above, 0), mytie);
+      uint64_t ties = ge & ~gt;
+      for (; drop > 0; --drop) {
+        const int hb = 63 - __builtin_clzll(ties);
+        ties &= ~(1ull << hb);
+        ge &= ~(1ull << hb);
+      }
+    } else if (total < K) {  // NaN logits only: fill with the lowest free ids
+      int freec[P];
+      const int myfree = __builtin_popcountll(valid & ~ge);
+#pragma unroll
+      for (int r = 0; r < P; ++r) freec[r] = __shfl(myfree, grp + r);
+      int below = 0;
+#pragma unroll
+      for (int r = 0; r < P; ++r) below += r < q ? freec[r] : 0;
+      int add = min(max(K - total - below, 0), myfree);
+      uint64_t fr = valid & ~ge;
+      for (; add > 0; --add) {
+        const uint64_t lo = fr & (~fr + 1);
+        fr &= ~lo;
+        ge |= lo;
+      }
+    }
+    const int kept = __builtin_popcountll(ge);
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      const int kr = __shfl(kept, grp + r);
+      base += r < q ? kr : 0;
+    }
+    if (live) {
+      const float vmax = b[0];
+      float ssum = 0.f;
+#pragma unroll
+      for (int i = 0; i < KM; ++i)
+        if (i < K) ssum += expf(b[i] - vmax);
+      const float inv = 1.0f / ssum;
+      uint64_t m = ge;
+      for (int slot = base; m != 0 && slot < K; ++slot) {
+        const int e = e0 + __builtin_ctzll(m);
+        m &= m - 1;
+        tei[t * K + slot] = e;
+        gates[t * K + slot] = expf(row[e] - vmax) * inv;
+        smap[e * T + tl] = (uint8_t)(slot + 1);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6;
+  const int nv = T >> 4;
+  for (int e = wave; e < E; e += 4) {
+    int c = 0;
+    for (int i = lane; i < nv; i += 64) {
+      const uint4 w = smap_v[(e * T >> 4) + i];
+      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = w;
+      c += nonzero_bytes(w.x) + nonzero_bytes(w.y) + nonzero_bytes(w.z) + nonzero_bytes(w.w);
+    }
+    c = wave_sum(c);
+    if (lane == 0) tilecnt[(int64_t)e * C + tile] = c;
+  }
+}
+
 // Step 1 for E <= 64: one thread per token with the token's logits in
 // registers (EV = E rounded up to a multiple of 4).  Top-K is K register
 // passes of an arg-max with ties to the lower id; no cross-lane traffic.
@@ -728,6 +888,33 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
       }
 #undef K1M_K
 #undef K1M
+    } else if (E <= 256 && K <= 8 && pl.T == 256) {
+      const size_t sh = (size_t)E * pl.T;
+#define K1W(PV, KV, VV)                                                                         \
+  hipLaunchKernelGGL((k1_route_wide<PV, KV, VV>), dim3(pl.C), dim3(256), sh, s, logits, L, E, K, \
+                     pl.T, pl.C, pl.Lpad, tei, gates, map, cnt)
+#define K1W_K(PV)                                                                               \
+  if (!rows_ok) {                                                                               \
+    K1W(PV, 8, false);                                                                          \
+  } else {                                                                                      \
+    switch (K) {                                                                                \
+      case 1: K1W(PV, 1, true); break;                                                          \
+      case 2: K1W(PV, 2, true); break;                                                          \
+      case 3: K1W(PV, 3, true); break;                                                          \
+      case 4: K1W(PV, 4, true); break;                                                          \
+      case 5: K1W(PV, 5, true); break;                                                          \
+      case 6: K1W(PV, 6, true); break;                                                          \
+      case 7: K1W(PV, 7, true); break;                                                          \
+      default: K1W(PV, 8, true); break;                                                         \
+    }                                                                                           \
+  }
+      if (E <= 128) {
+        K1W_K(2)
+      } else {
+        K1W_K(4)
+      }
+#undef K1W_K
+#undef K1W
     } else if (rows_ok && E <= 64) {
       const size_t sh = (size_t)E * pl.T;
 #define MOE_K1R(EVV)                                                                            \
