@@ -78,6 +78,13 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// p advanced by a 32-bit byte offset (lets the compiler address with a
+// scalar base and a 32-bit vector offset)
+template <typename T>
+__device__ __forceinline__ T* byte_off(T* p, uint32_t bytes) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + bytes);
+}
+
 __device__ __forceinline__ uint4 sel16(bool ok, uint4 v) {
   return ok ? v : make_uint4(0, 0, 0, 0);
 }
@@ -490,14 +497,20 @@ __device__ __forceinline__ void TLoaderD::setup(const char* b0, const char* b1, 
 
 template <typename T>
 __device__ __forceinline__ float silu_of(float a);
+// bf16 results: the hardware reciprocal (1 ulp) replaces the IEEE division,
+// far below the bf16 rounding of everything these values feed.
 template <>
-__device__ __forceinline__ float silu_of<bf16_t>(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu_of<bf16_t>(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 template <>
 __device__ __forceinline__ float silu_of<float>(float a) { return a / (1.0f + expf(-a)); }
 template <typename T>
 __device__ __forceinline__ float sigm_of(float a);
 template <>
-__device__ __forceinline__ float sigm_of<bf16_t>(float a) { return 1.0f / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float sigm_of<bf16_t>(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 template <>
 __device__ __forceinline__ float sigm_of<float>(float a) { return 1.0f / (1.0f + expf(-a)); }
 
@@ -678,7 +691,9 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   int4 ds;
   int ntile;
   if (!route_tile(ra, ds, ntile)) return;
-  const int e = ds.x, rb = ds.y, re = ds.z;
+  // the tile descriptor is uniform: keep it in scalar registers
+  const int e = __builtin_amdgcn_readfirstlane(ds.x);
+  const int rb = __builtin_amdgcn_readfirstlane(ds.y), re = __builtin_amdgcn_readfirstlane(ds.z);
   const int n0 = ntile * (DUAL ? 128 : 256);
 
   KLoaderD<T> la;
@@ -701,20 +716,25 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   Acc acc;
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
 
+  // tile-relative 32-bit offsets from the tile's first row (at most 256 rows)
+  const int64_t tb = (int64_t)rb * h;
+  T* At = A + tb;
+  T* Bt = DUAL ? B + tb : nullptr;
+  T* Gt = G + tb;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int p = rb + acc_row(mt, i);
-      if (p >= re) continue;
+      const int r = acc_row(mt, i);
+      if (rb + r >= re) continue;
       if (DUAL) {
         const int c = n0 + dual_col(acc_col(0));
         if (c < h) {
           const float a = acc.c[mt][0][i], b = acc.c[mt][1][i];
-          const int64_t o = (int64_t)p * h + c;
-          Elem<T>::store(A + o, a);
-          Elem<T>::store(B + o, b);
-          Elem<T>::store(G + o, silu_of<T>(a) * b);
+          const uint32_t o = (uint32_t)(r * h + c) * (uint32_t)sizeof(T);  // bytes
+          Elem<T>::store(byte_off(At, o), a);
+          Elem<T>::store(byte_off(Bt, o), b);
+          Elem<T>::store(byte_off(Gt, o), silu_of<T>(a) * b);
         }
       } else {
 #pragma unroll
@@ -722,9 +742,9 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
           const int c = n0 + acc_col(nt);
           if (c < h) {
             const float a = acc.c[mt][nt][i];
-            const int64_t o = (int64_t)p * h + c;
-            Elem<T>::store(A + o, a);
-            Elem<T>::store(G + o, silu_of<T>(a));
+            const uint32_t o = (uint32_t)(r * h + c) * (uint32_t)sizeof(T);  // bytes
+            Elem<T>::store(byte_off(At, o), a);
+            Elem<T>::store(byte_off(Gt, o), silu_of<T>(a));
           }
         }
       }

@@ -21,10 +21,8 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint
 
 // float32 -> bfloat16, round to nearest even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // round to nearest even (gfx950: one v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename T> struct Elem;
