@@ -753,50 +753,115 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
 }
 
 // Slot-pass epilogue: out/acc row t = s_t[row] (-1: no row), scale s_g[row].
-//   mode 0: only pass (K == 1): out = v
-//   mode 1: first pass:  acc = v
-//   mode 2: middle pass: acc += v
-//   mode 3: last pass:   out = acc + v
-// For float32 outputs `acc` is the output itself (modes 1/2 only).  The
-// accumulator values of one MFMA row block are all loaded before any is
-// used, from a valid address when the element is absent.
+//   MODE 0: only pass (K == 1): out = v
+//   MODE 1: first pass:  acc = v
+//   MODE 2: middle pass: acc += v
+//   MODE 3: last pass:   out = acc + v
+// For float32 outputs `acc` is the output itself (modes 1/2 only).
+//
+// The tile goes through LDS in four quarters of 64 rows (MFMA row block q of
+// both wavefront rows), 64 KB of float32 each, alternating between the two
+// halves of the LDS, so that every thread then owns eight whole 16-byte
+// chunks (four columns) of a quarter: accumulator loads and stores are 16
+// bytes per lane and a wavefront covers one 1 KB row.  Quarter q is combined
+// while quarter q + 1 is parked and the accumulator loads of quarter q + 2
+// are in flight.  d % 8 == 0 makes every chunk all in or all out.
+constexpr int CCH = 8;  // chunks per thread per quarter: 64 rows x 64 chunks / NT
+
+// Chunk j of a quarter, for wavefront w = threadIdx.x / 64: LDS row 8j + w,
+// tile row cq(j) + 32 qq + w, columns 4 (threadIdx.x % 64) .. + 3.  Only w
+// and the lane vary at run time, so every chunk's LDS address is a constant
+// offset from one base.
+__device__ __forceinline__ constexpr int cq(int j) { return (j >> 2) * 128 + (j & 3) * 8; }
+
+template <int MODE>
+__device__ __forceinline__ void combine_load(const int32_t* s_tw, int qq, int c, int d,
+                                             const float* __restrict__ accb, float4 prev[CCH]) {
+  if constexpr (MODE >= 2) {
+#pragma unroll
+    for (int j = 0; j < CCH; ++j) {
+      const int t = s_tw[cq(j) + 32 * qq];
+      const bool ok = t >= 0 && c < d;
+      // absent chunks read the (valid) first chunk and are never used
+      const int64_t o = (int64_t)(ok ? t : 0) * d + (ok ? c : 0);
+      prev[j] = *reinterpret_cast<const float4*>(accb + o);
+    }
+  }
+}
+
+// MFMA row block qq of every wavefront -> LDS rows [64][256] f32 (buffer sb)
+__device__ __forceinline__ void combine_park(const Acc& acc, float* sb, int qq) {
+  const int lane = threadIdx.x & 63;
+  // this lane's first element; the others sit at constant offsets from it
+  float* base = sb + (wave_m() * 32 + (lane >> 5) * 4) * 256 + acc_col(0);
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      base[((i >> 2) * 8 + (i & 3)) * 256 + nt * 32] = acc.c[qq][nt][i];
+}
+
+template <typename T, int MODE>
+__device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t* s_tw,
+                                                const float* s_gw, int qq, int c, int d,
+                                                const float4 prev[CCH], T* __restrict__ out,
+                                                float* __restrict__ accb) {
+#pragma unroll
+  for (int j = 0; j < CCH; ++j) {
+    const int t = s_tw[cq(j) + 32 * qq];
+    if (t < 0 || c >= d) continue;
+    const float g = s_gw[cq(j) + 32 * qq];
+    const float4 a = *reinterpret_cast<const float4*>(sbw + j * 8 * 256);
+    float4 v = make_float4(g * a.x, g * a.y, g * a.z, g * a.w);
+    if constexpr (MODE >= 2)
+      v = make_float4(prev[j].x + v.x, prev[j].y + v.y, prev[j].z + v.z, prev[j].w + v.w);
+    const int64_t o = (int64_t)t * d + c;
+    if constexpr (MODE == 1 || MODE == 2) {
+      *reinterpret_cast<float4*>(accb + o) = v;
+    } else if constexpr (std::is_same<T, float>::value) {
+      *reinterpret_cast<float4*>(out + o) = v;
+    } else {
+      const uint2 w = make_uint2((uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                                 (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+      *reinterpret_cast<uint2*>(out + o) = w;
+    }
+  }
+}
+
+// Called after the main loop's final barrier (LDS free, s_t / s_g visible).
+template <typename T, int MODE>
+__device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, const int32_t* s_t,
+                                                 const float* s_g, int n0, int d,
+                                                 T* __restrict__ out, float* __restrict__ accb) {
+  const int w = threadIdx.x >> 6, cl = (threadIdx.x & 63) * 4;
+  const int c = n0 + cl;
+  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + 64 * 256};
+  const int32_t* s_tw = s_t + w;
+  const float* s_gw = s_g + w;
+  float4 p[2][CCH];
+  combine_load<MODE>(s_tw, 0, c, d, accb, p[0]);
+  combine_park(acc, sb[0], 0);
+  combine_load<MODE>(s_tw, 1, c, d, accb, p[1]);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    // buffer (q + 1) & 1 was last read before the previous barrier
+    if (q + 1 < MT) combine_park(acc, sb[(q + 1) & 1], q + 1);
+    combine_quarter<T, MODE>(sb[q & 1] + w * 256 + cl, s_tw, s_gw, q, c, d, p[q & 1], out, accb);
+    if (q + 2 < MT) combine_load<MODE>(s_tw, q + 2, c, d, accb, p[q & 1]);
+    if (q + 1 < MT) __syncthreads();
+  }
+}
+
 template <typename T>
-__device__ __forceinline__ void combine_epilogue(const Acc& acc, const int64_t* s_t,
+__device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, const int32_t* s_t,
                                                  const float* s_g, int n0, int d, int mode,
                                                  T* __restrict__ out, float* __restrict__ accb) {
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float prev[16][NTL];
-    if (mode >= 2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t t = s_t[acc_row(mt, i)];
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-          const int c = n0 + acc_col(nt);
-          const bool ok = t >= 0 && c < d;
-          const float x = accb[ok ? t * d + c : 0];
-          prev[i][nt] = ok ? x : 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = acc_row(mt, i);
-      const int64_t t = s_t[row];
-      const float g = s_g[row];
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) {
-        const int c = n0 + acc_col(nt);
-        if (t < 0 || c >= d) continue;
-        const int64_t o = t * d + c;
-        const float v = g * acc.c[mt][nt][i];
-        if (mode == 0) Elem<T>::store(out + o, v);
-        else if (mode == 1) accb[o] = v;
-        else if (mode == 2) accb[o] = prev[i][nt] + v;
-        else Elem<T>::store(out + o, prev[i][nt] + v);
-      }
-    }
+  switch (mode) {
+    case 0: combine_epilogue<T, 0>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 1: combine_epilogue<T, 1>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 2: combine_epilogue<T, 2>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    default: combine_epilogue<T, 3>(acc, smem, s_t, s_g, n0, d, out, accb); break;
   }
 }
 
@@ -812,7 +877,7 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
                                                          T* __restrict__ y,
                                                          float* __restrict__ yacc) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  __shared__ int64_t s_t[TBM];
+  __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
@@ -822,11 +887,11 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   const int n0 = ntile * 256;
   if (threadIdx.x < TBM) {
     const int li = rb + threadIdx.x;
-    int64_t t = -1;
+    int32_t t = -1;
     float g = 0.f;
     if (li < re) {
       t = eti[list[li]];
-      g = gates[t * K + k];
+      g = gates[(int64_t)t * K + k];
     }
     s_t[threadIdx.x] = t;
     s_g[threadIdx.x] = g;
@@ -843,7 +908,7 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   Acc acc;
   gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_epilogue<T>(acc, s_t, s_g, n0, d, mode, y, yacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, y, yacc);
 }
 
 // B1: dG = gate * (dy[t] W2_e^T) per route; epilogue recomputes SiLU from
@@ -1134,7 +1199,7 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
                                                int mode, T* __restrict__ dx,
                                                float* __restrict__ dxacc) {
   __shared__ __attribute__((aligned(16))) char smem[LDSB];
-  __shared__ int64_t s_t[TBM];
+  __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
@@ -1145,7 +1210,7 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
   const int klen = DUAL ? 2 * h : h;
   if (threadIdx.x < TBM) {
     const int li = rb + threadIdx.x;
-    s_t[threadIdx.x] = li < re ? (int64_t)eti[list[li]] : -1;
+    s_t[threadIdx.x] = li < re ? eti[list[li]] : -1;
     s_g[threadIdx.x] = 1.0f;
   }
 
@@ -1162,7 +1227,7 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
   Acc acc;
   gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_epilogue<T>(acc, s_t, s_g, n0, d, mode, dx, dxacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, dx, dxacc);
 }
 
 // ------------------------------------------------------------------ host
