@@ -676,6 +676,73 @@ __device__ __forceinline__ bool route_tile(const RouteArgs& ra, int4& ds, int& n
   return ds.x >= 0;
 }
 
+// ------------------------------------------------------------------ staged epilogues
+// The epilogues below pass the accumulator tile through LDS a quarter at a
+// time: MFMA row block q of both wavefront rows (tile rows 32q .. 32q + 31
+// and 128 + 32q .. 128 + 32q + 31) as [64][256] float32 (64 KB), alternating
+// between the two halves of the LDS.  LDS row r of quarter q is tile row
+// (r / 32) * 128 + 32 q + r % 32.  Each thread then owns whole chunks of a
+// row, so global loads and stores are 16 bytes per lane.
+
+// MFMA row block qq of every wavefront -> LDS rows [64][256] f32 (buffer sb)
+__device__ __forceinline__ void park_quarter(const Acc& acc, float* sb, int qq) {
+  const int lane = threadIdx.x & 63;
+  // this lane's first element; the others sit at constant offsets from it
+  float* base = sb + (wave_m() * 32 + (lane >> 5) * 4) * 256 + acc_col(0);
+#pragma unroll
+  for (int nt = 0; nt < NTL; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      base[((i >> 2) * 8 + (i & 3)) * 256 + nt * 32] = acc.c[qq][nt][i];
+}
+
+__device__ __forceinline__ int quarter_row(int qq, int r) { return (r >> 5) * 128 + qq * 32 + (r & 31); }
+
+// Eight consecutive elements of a row, raw (as loaded) and as float32.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float v[8]) const {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(q[k] << 16);
+      v[2 * k + 1] = __uint_as_float(q[k] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
+  uint32_t q[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) q[k] = (uint32_t)f2bf(v[2 * k]) | ((uint32_t)f2bf(v[2 * k + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(q[0], q[1], q[2], q[3]);
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// eight float32 from LDS (16-byte aligned)
+__device__ __forceinline__ void lds8(const float* p, float v[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // F1: [A | B] = X W1 [| X W3] with X gathered by expert_token_indices;
 // epilogue writes A, B (checkpoint) and G = SiLU(A) [* B].
 // W1T, W3T: [E, h, d] (transposed weights).
@@ -759,13 +826,11 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
 //   MODE 3: last pass:   out = acc + v
 // For float32 outputs `acc` is the output itself (modes 1/2 only).
 //
-// The tile goes through LDS in four quarters of 64 rows (MFMA row block q of
-// both wavefront rows), 64 KB of float32 each, alternating between the two
-// halves of the LDS, so that every thread then owns eight whole 16-byte
-// chunks (four columns) of a quarter: accumulator loads and stores are 16
-// bytes per lane and a wavefront covers one 1 KB row.  Quarter q is combined
-// while quarter q + 1 is parked and the accumulator loads of quarter q + 2
-// are in flight.  d % 8 == 0 makes every chunk all in or all out.
+// Staged quarter by quarter (see park_quarter): each thread owns eight
+// 16-byte chunks (four columns) of a quarter, so a wavefront covers one 1 KB
+// accumulator row.  Quarter q is combined while quarter q + 1 is parked and
+// the accumulator loads of quarter q + 2 are in flight.  d % 8 == 0 makes
+// every chunk all in or all out.
 constexpr int CCH = 8;  // chunks per thread per quarter: 64 rows x 64 chunks / NT
 
 // Chunk j of a quarter, for wavefront w = threadIdx.x / 64: LDS row 8j + w,
@@ -787,18 +852,6 @@ __device__ __forceinline__ void combine_load(const int32_t* s_tw, int qq, int c,
       prev[j] = *reinterpret_cast<const float4*>(accb + o);
     }
   }
-}
-
-// MFMA row block qq of every wavefront -> LDS rows [64][256] f32 (buffer sb)
-__device__ __forceinline__ void combine_park(const Acc& acc, float* sb, int qq) {
-  const int lane = threadIdx.x & 63;
-  // this lane's first element; the others sit at constant offsets from it
-  float* base = sb + (wave_m() * 32 + (lane >> 5) * 4) * 256 + acc_col(0);
-#pragma unroll
-  for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      base[((i >> 2) * 8 + (i & 3)) * 256 + nt * 32] = acc.c[qq][nt][i];
 }
 
 template <typename T, int MODE>
@@ -840,13 +893,13 @@ __device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, con
   const float* s_gw = s_g + w;
   float4 p[2][CCH];
   combine_load<MODE>(s_tw, 0, c, d, accb, p[0]);
-  combine_park(acc, sb[0], 0);
+  park_quarter(acc, sb[0], 0);
   combine_load<MODE>(s_tw, 1, c, d, accb, p[1]);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < MT; ++q) {
     // buffer (q + 1) & 1 was last read before the previous barrier
-    if (q + 1 < MT) combine_park(acc, sb[(q + 1) & 1], q + 1);
+    if (q + 1 < MT) park_quarter(acc, sb[(q + 1) & 1], q + 1);
     combine_quarter<T, MODE>(sb[q & 1] + w * 256 + cl, s_tw, s_gw, q, c, d, p[q & 1], out, accb);
     if (q + 2 < MT) combine_load<MODE>(s_tw, q + 2, c, d, accb, p[q & 1]);
     if (q + 1 < MT) __syncthreads();
@@ -911,12 +964,97 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, y, yacc);
 }
 
+// B1 epilogue on 8-column chunks: dG = gate * acc; with s = sigmoid(A),
+// SiLU(A) = A s and SiLU'(A) = s (1 + A (1 - s)): dA = dG [* B] * SiLU'(A)
+// and dB = dG * SiLU(A) are written over A and B, Gs = gate * SiLU(A) [* B].
+// bf16: the checkpoint loads of quarter q + 1 are in flight while quarter q
+// is processed.  ROUTER: dgp[p * nN + ntile] = sum over the tile's columns
+// of acc * SiLU(A) [* B]; a row's 32 chunk lanes are summed by a fixed
+// butterfly, so the value does not depend on timing.
+template <typename T, bool DUAL, bool ROUTER>
+__device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const float* s_g, int rb,
+                                            int re, int n0, int h, int nN, int ntile,
+                                            T* __restrict__ A, T* __restrict__ B,
+                                            T* __restrict__ Gs, float* __restrict__ dgp) {
+  constexpr int CPT = 4;                    // chunks per thread per quarter (32 per row)
+  constexpr bool PF = sizeof(T) == 2;       // prefetch the next quarter
+  constexpr int NB = PF ? 2 : 1;
+  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + 64 * 256};
+  const int ch = threadIdx.x & 31, r0 = threadIdx.x >> 5;  // rows r0 + 16 j
+  const int c = n0 + ch * 8;
+  Raw8<T> xa[NB][CPT], xb[NB][CPT];
+  auto load = [&](int q, int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int p = rb + quarter_row(q, r0 + 16 * j);
+      const bool ok = p < re && c < h;
+      // absent chunks read the (valid) first chunk and are never used
+      const int64_t o = ok ? (int64_t)p * h + c : 0;
+      xa[buf][j].load(A + o);
+      if (DUAL) xb[buf][j].load(B + o);
+    }
+  };
+  if (PF) load(0, 0);
+  park_quarter(acc, sb[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (PF) load(1, NB - 1);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    // buffer (q + 1) & 1 was last read before the previous barrier
+    if (q + 1 < MT) park_quarter(acc, sb[(q + 1) & 1], q + 1);
+    if (!PF) load(q, 0);
+    const int buf = PF ? (q & 1) : 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int r = r0 + 16 * j;
+      const int row = quarter_row(q, r);
+      const int p = rb + row;
+      float rdot = 0.f;
+      if (p < re && c < h) {
+        const int64_t o = (int64_t)p * h + c;
+        const float gp = s_g[row];
+        float v[8], a[8], b[8], da[8], db[8], gs[8];
+        lds8(sb[q & 1] + r * 256 + ch * 8, v);
+        xa[buf][j].get(a);
+        if (DUAL) xb[buf][j].get(b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float dg = gp * v[k];
+          const float sg = sigm_of<T>(a[k]);
+          const float sl = a[k] * sg;
+          const float ds_ = sg * (1.0f + a[k] * (1.0f - sg));
+          if (DUAL) {
+            da[k] = dg * b[k] * ds_;
+            db[k] = dg * sl;
+            gs[k] = gp * sl * b[k];
+            if (ROUTER) rdot += v[k] * (sl * b[k]);
+          } else {
+            da[k] = dg * ds_;
+            gs[k] = gp * sl;
+            if (ROUTER) rdot += v[k] * sl;
+          }
+        }
+        store8(A + o, da);
+        if (DUAL) store8(B + o, db);
+        store8(Gs + o, gs);
+      }
+      if (ROUTER) {
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) rdot += __shfl_xor(rdot, m);
+        if (ch == 0 && p < re) dgp[(int64_t)p * nN + ntile] = rdot;
+      }
+    }
+    if (PF && q + 2 < MT) load(q + 2, q & 1);
+    if (q + 1 < MT) __syncthreads();
+  }
+}
+
 // B1: dG = gate * (dy[t] W2_e^T) per route; epilogue recomputes SiLU from
 // the checkpoint and writes dA, dB over A, B and Gs = gate * G.  ROUTER: it
 // also leaves, for every route row p, the tile's share of the router
 // gradient's <dy[t] W2_e^T, G[p]> (= <dy[t], O[p]>, O the route's un-gated
-// output) in dgp[p * nN + ntile]: each thread's products are summed over its
-// columns, parked in LDS, and added per row in a fixed order.
+// output) in dgp[p * nN + ntile].
 template <typename T, bool DUAL, bool ROUTER>
 __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __restrict__ dy,
                                                       const T* __restrict__ W2,
@@ -950,75 +1088,7 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
   __syncthreads();
 
-  // LDS after the main loop (ROUTER): [256 rows][128 column lanes] of
-  // row-dot products
-  float* s_part = reinterpret_cast<float*>(smem);
-  const int pcol = wave_n() * 32 + ((threadIdx.x & 63) & 31);
-  constexpr int IB = 16;  // rows of checkpoint loads in flight
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i0 = 0; i0 < 16; i0 += IB) {
-      float av[IB][NTL], bv[IB][NTL];
-#pragma unroll
-      for (int ii = 0; ii < IB; ++ii) {
-        const int p = rb + acc_row(mt, i0 + ii);
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-          const int c = n0 + acc_col(nt);
-          const bool ok = p < re && c < h;
-          const int64_t o = ok ? (int64_t)p * h + c : 0;
-          av[ii][nt] = Elem<T>::load(A + o);
-          bv[ii][nt] = DUAL ? Elem<T>::load(B + o) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int ii = 0; ii < IB; ++ii) {
-        const int i = i0 + ii;
-        const int row = acc_row(mt, i);
-        const int p = rb + row;
-        const float gp = s_g[row];
-        float rdot = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-          const int c = n0 + acc_col(nt);
-          if (p >= re || c >= h) continue;
-          const int64_t o = (int64_t)p * h + c;
-          const float dg = gp * acc.c[mt][nt][i];
-          const float a = av[ii][nt];
-          const float s = sigm_of<T>(a);
-          const float sl = a * s;
-          const float ds_ = s * (1.0f + a * (1.0f - s));
-          if (DUAL) {
-            const float b = bv[ii][nt];
-            Elem<T>::store(A + o, dg * b * ds_);
-            Elem<T>::store(B + o, dg * sl);
-            Elem<T>::store(Gs + o, gp * sl * b);
-            if (ROUTER) rdot += acc.c[mt][nt][i] * (sl * b);
-          } else {
-            Elem<T>::store(A + o, dg * ds_);
-            Elem<T>::store(Gs + o, gp * sl);
-            if (ROUTER) rdot += acc.c[mt][nt][i] * sl;
-          }
-        }
-        if (ROUTER) s_part[row * 128 + pcol] = rdot;
-      }
-    }
-  }
-  if (ROUTER) {
-    __syncthreads();
-    // each row is read by two adjacent lanes (one half each), starting at a
-    // lane-dependent column so that a wavefront's reads hit 64 distinct banks;
-    // a given row is always summed by the same lane in the same order
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int rot = (row + 32 * half) & 63;
-    float v = 0.f;
-    for (int j = 0; j < 64; ++j) v += s_part[row * 128 + half * 64 + ((j + rot) & 63)];
-    const float other = __shfl_xor(v, 1);
-    const float tot = half == 0 ? v + other : other + v;  // same order in both lanes
-    const int p = rb + row;
-    if (half == 0 && p < re) dgp[(int64_t)p * ra.nN + ntile] = tot;
-  }
+  b1_epilogue<T, DUAL, ROUTER>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
 // Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
