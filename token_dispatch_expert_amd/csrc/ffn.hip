@@ -365,62 +365,64 @@ struct Acc {
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) >> 2; }
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) & 3; }
 
+// MFMA fragments of two k-chunks (16 k each).  A k-tile's last chunk stays
+// in slot 1 past the barrier that ends the tile: its MFMAs issue at the start
+// of the next tile, after that tile's first fragment reads, so the LDS read
+// latency after the barrier is covered.
+struct Frags {
+  uint4 a[2][MT], b[2][NTL];
+};
+
 template <typename T>
-__device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& acc) {
+__device__ __forceinline__ void mma_chunk(const uint4 (&a)[MT], const uint4 (&b)[NTL], Acc& acc) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[mt], b[nt], acc.c[mt][nt]);
+}
+
+// fragments of k-chunk kc (k-tiles with k contiguous per LDS row)
+__device__ __forceinline__ void read_chunk(const char* As, const char* Bs, int kc, uint4 (&a)[MT],
+                                           uint4 (&b)[NTL]) {
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
   const int r = lane & 31, g = lane >> 5;
-  // Fragments of k-chunk kc + 1 are read while the MFMAs of kc issue.
-  uint4 a[2][MT], b[2][NTL];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    a[0][mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, g));
+    a[mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, kc * 2 + g));
 #pragma unroll
   for (int nt = 0; nt < NTL; ++nt)
-    b[0][nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, g));
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
-    const int cb = kc & 1, nb = cb ^ 1;
-    if (kc < 3) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[nb][mt] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 128 + mt * 32 + r, (kc + 1) * 2 + g));
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt)
-        b[nb][nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, (kc + 1) * 2 + g));
-    }
-    // keep the reads above ahead of this chunk's MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) acc.c[mt][nt] = mfma_k8<T>(a[cb][mt], b[cb][nt], acc.c[mt][nt]);
-  }
+    b[nt] = *reinterpret_cast<const uint4*>(Bs + lds_off(wn * 64 + nt * 32 + r, kc * 2 + g));
 }
 
-// One k-tile of MFMAs on two TLoaderD tiles (bf16).
-__device__ __forceinline__ void mma_ktile_tr(const char* As, const char* Bs, Acc& acc) {
+// fragments of k-chunk kc from [k][position] tiles (transposing reads, bf16)
+__device__ __forceinline__ void read_chunk_tr(const char* As, const char* Bs, int kc,
+                                              uint4 (&a)[MT], uint4 (&b)[NTL]) {
   const int wm = wave_m(), wn = wave_n();
-  uint4 a[2][MT], b[2][NTL];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) a[0][mt] = tr_fragment(As, wm * 128 + mt * 32, 0);
+  for (int mt = 0; mt < MT; ++mt) a[mt] = tr_fragment(As, wm * 128 + mt * 32, kc * 16);
 #pragma unroll
-  for (int nt = 0; nt < NTL; ++nt) b[0][nt] = tr_fragment(Bs, wn * 64 + nt * 32, 0);
+  for (int nt = 0; nt < NTL; ++nt) b[nt] = tr_fragment(Bs, wn * 64 + nt * 32, kc * 16);
+}
+
+// One k-tile of MFMAs.  pending: slot 1 holds the previous tile's last
+// chunk.  On return slot 1 holds this tile's last chunk, not yet multiplied.
+template <typename T, bool TR>
+__device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& acc, Frags& f,
+                                          bool pending) {
+  if constexpr (TR) read_chunk_tr(As, Bs, 0, f.a[0], f.b[0]);
+  else read_chunk(As, Bs, 0, f.a[0], f.b[0]);
+  // keep the reads above ahead of the MFMAs below
+  __builtin_amdgcn_sched_barrier(0);
+  if (pending) mma_chunk<T>(f.a[1], f.b[1], acc);
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
+  for (int kc = 0; kc < 3; ++kc) {
     const int cb = kc & 1, nb = cb ^ 1;
-    if (kc < 3) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a[nb][mt] = tr_fragment(As, wm * 128 + mt * 32, (kc + 1) * 16);
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt) b[nb][nt] = tr_fragment(Bs, wn * 64 + nt * 32, (kc + 1) * 16);
-    }
+    // fragments of k-chunk kc + 1 are read while the MFMAs of kc issue
+    if constexpr (TR) read_chunk_tr(As, Bs, kc + 1, f.a[nb], f.b[nb]);
+    else read_chunk(As, Bs, kc + 1, f.a[nb], f.b[nb]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTL; ++nt)
-        acc.c[mt][nt] = mfma_k8<bf16_t>(a[cb][mt], b[cb][nt], acc.c[mt][nt]);
+    mma_chunk<T>(f.a[cb], f.b[cb], acc);
   }
 }
 
@@ -440,6 +442,7 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
   if constexpr (DB) lb.issue(0, smem + OPB); else { lb.fetch(0); lb.store(smem + OPB); }
   if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  Frags f;
   for (int kt = 0; kt < nk; ++kt) {
     char* cur = smem + (kt & 1) * STAGE;
     char* nxt = smem + ((kt + 1) & 1) * STAGE;
@@ -448,8 +451,7 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
       if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
       if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
     }
-    if constexpr (TR) mma_ktile_tr(cur, cur + OPB, acc);
-    else mma_ktile<T>(cur, cur + OPB, acc);
+    mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
     if (more) {
       if constexpr (!DA) la.store(nxt);
       if constexpr (!DB) lb.store(nxt + OPB);
@@ -457,6 +459,7 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
     if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  mma_chunk<T>(f.a[1], f.b[1], acc);
 }
 
 // Position of accumulator element i of MFMA tile (mt, nt) inside the
