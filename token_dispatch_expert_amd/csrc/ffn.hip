@@ -1142,15 +1142,19 @@ struct WeightArgs {           // weight-gradient tiles: E x nM x nN
 // one expert round-robin over the XCDs: a tile's cost is its expert's route
 // count, so giving each XCD a contiguous run of experts (as the route-major
 // products do) would pile the heaviest experts onto one XCD when loads are
-// skewed.
+// skewed.  Inside an expert the faster-running tile index is the one whose
+// count is a multiple of the 8 XCDs (N if both are), so that every tile an
+// XCD receives from an expert shares that XCD's operand block on the other
+// side (same M block, or same N block) and reads it from its own L2.
 __device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& mi, int& ni) {
   const int64_t lid = blockIdx.x;
   const int64_t per_e = (int64_t)wa.nM * wa.nN;
   if (lid >= (int64_t)wa.E * per_e) return false;
   e = (int)(lid / per_e);
   const int rem = (int)(lid % per_e);
-  mi = rem / wa.nN;
-  ni = rem % wa.nN;
+  const bool mfast = (wa.nN & 7) != 0 && (wa.nM & 7) == 0;
+  mi = mfast ? rem % wa.nM : rem / wa.nN;
+  ni = mfast ? rem / wa.nM : rem % wa.nN;
   return true;
 }
 
