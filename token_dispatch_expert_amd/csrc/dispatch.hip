@@ -612,6 +612,7 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
   __shared__ int s_run[65];  // start of each expert's run inside the tile
   __shared__ int s_tok[MAXE];
   __shared__ int s_pos[MAXE];
+  __shared__ int s_tim[MAXE];  // the tile's token_index_map rows, written out contiguously
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   int tile;
@@ -661,19 +662,22 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
   }
   __syncthreads();
   if (t < L) {
-    for (int k = 0; k < K && m != 0; ++k) {
-      const int e = lowest_bit(m);
-      m &= m - 1;
-      const uint64_t ce = s_col[wave][e];
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ce >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ce, 0));
-      const int pos = s_base[wave][e] + below;
-      const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
-      if (lp < MAXE) {  // always true when the masks hold K bits each
-        s_tok[lp] = (int32_t)t;
-        s_pos[lp] = pos;
+    for (int k = 0; k < K; ++k) {
+      int pos = -1;  // (a mask with fewer than K bits leaves -1)
+      if (m != 0) {
+        const int e = lowest_bit(m);
+        m &= m - 1;
+        const uint64_t ce = s_col[wave][e];
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ce >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)ce, 0));
+        pos = s_base[wave][e] + below;
+        const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
+        if (lp < MAXE) {  // always true when the masks hold K bits each
+          s_tok[lp] = (int32_t)t;
+          s_pos[lp] = pos;
+        }
       }
-      tim[t * K + k] = pos;
+      s_tim[tid * K + k] = pos;
     }
   }
   __syncthreads();
@@ -683,43 +687,68 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
     const int pos = s_pos[j];
     if (pos < R) eti[pos] = s_tok[j];  // always true when the masks hold K bits each
   }
+  // rows t0 .. t0 + 255 of token_index_map are one contiguous run
+  const int64_t t0 = (int64_t)tile * 256;
+  const int nt = (int)min((int64_t)256, L - t0) * K;
+  for (int j = tid; j < nt; j += 256) tim[t0 * K + j] = s_tim[j];
 }
 
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
 // row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
 // the row sum when total is not null.  With G > 1 the input rows hold G
 // consecutive counts per entry ([rows][C * G]), which are added first.
+// A pass covers V rounds of 256 consecutive entries, one entry per thread
+// and round, so that loads and stores are contiguous across lanes; each
+// wavefront scans its 64 entries of a round, and one barrier per pass
+// shares the 4 V wavefront sums, scanned in (round, wavefront) order.
 template <int G>
 __global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt, int C,
                                                 int64_t row_offset, int32_t* __restrict__ base,
                                                 int32_t* __restrict__ total) {
-  constexpr int V = 16;  // consecutive entries per thread and pass
-  __shared__ int scratch[4];
+  constexpr int V = 16;  // rounds per pass; V * 4 wavefront sums == one wavefront
+  static_assert(V * 4 == kWave, "one lane per wavefront sum");
+  __shared__ int s_w[V * 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x;
   const int32_t* in = cnt + (int64_t)r * C * G;
   int32_t* out = base + (int64_t)r * C;
   int run = 0;
   for (int c0 = 0; c0 < C; c0 += 256 * V) {
-    const int cb = c0 + threadIdx.x * V;
     int x[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      x[i] = 0;
+    for (int j = 0; j < V; ++j) {
+      const int c = c0 + j * 256 + threadIdx.x;
+      x[j] = 0;
+      if (c < C) {
+        if constexpr (G == 4) {
+          const int4 q = *reinterpret_cast<const int4*>(in + (int64_t)c * 4);
+          x[j] = q.x + q.y + q.z + q.w;
+        } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) x[i] += cb + i < C ? in[(int64_t)(cb + i) * G + g] : 0;
+          for (int g = 0; g < G; ++g) x[j] += in[(int64_t)c * G + g];
+        }
+      }
     }
-    int sum = 0;
+    int ex[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) sum += x[i];
-    int tot;
-    int ex = block256_incl_scan(sum, scratch, &tot) - sum;
+    for (int j = 0; j < V; ++j) {
+      const int inc = wave_incl_scan(x[j], lane);
+      ex[j] = inc - x[j];
+      if (lane == 63) s_w[j * 4 + wave] = inc;
+    }
+    __syncthreads();
+    const int wv = s_w[lane];
+    const int wex = wave_incl_scan(wv, lane) - wv;  // before (round, wave) = lane
+    const int ptot = __shfl(wex + wv, 63);
     const int64_t add = r * row_offset + run;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      if (cb + i < C) out[cb + i] = (int32_t)(add + ex);
-      ex += x[i];
+    for (int j = 0; j < V; ++j) {
+      const int c = c0 + j * 256 + threadIdx.x;
+      const int before = __shfl(wex, j * 4 + wave);
+      if (c < C) out[c] = (int32_t)(add + before + ex[j]);
     }
-    run += tot;
+    run += ptot;
+    __syncthreads();  // s_w is rewritten by the next pass
   }
   if (total != nullptr && threadIdx.x == 0) total[r] = run;
 }
