@@ -667,13 +667,28 @@ struct RouteArgs {            // row tiles over routes or slot-pass lists
   int64_t ntiles;             // upper bound, rows of the grid
   int nN;                     // column tiles
   const char* zero;           // 16 zero bytes (workspace)
+  int gm;                     // row tiles per window (1: row by row)
 };
 
+// Launch size of a route-major GEMM: whole windows, a multiple of the 8 XCDs.
+static int64_t route_grid(const RouteArgs& ra) {
+  const int64_t rows = (ra.ntiles + ra.gm - 1) / ra.gm * ra.gm;
+  return (rows * ra.nN + 7) / 8 * 8;
+}
+
 // Tile coordinates of a route-major GEMM workgroup; false if it has no work.
+// Each XCD takes a contiguous run of logical tiles (its own L2).  Inside a
+// run, windows of gm row tiles are swept column tile by column tile, the
+// row tile running fastest: with gm = 4 the 32 workgroups an XCD runs at
+// once share four row tiles of A and eight column tiles of B, instead of
+// three and eleven row by row for a dual tile of h = 1408 (eleven column
+// tiles).
 __device__ __forceinline__ bool route_tile(const RouteArgs& ra, int4& ds, int& ntile) {
   const int64_t lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t mtile = lid / ra.nN;
-  ntile = (int)(lid % ra.nN);
+  const int64_t wsz = (int64_t)ra.gm * ra.nN;
+  const int64_t win = lid / wsz, r = lid % wsz;
+  const int64_t mtile = win * ra.gm + r % ra.gm;
+  ntile = (int)(r / ra.gm);
   if (mtile >= ra.ntiles) return false;
   ds = ra.tiles[mtile];
   return ds.x >= 0;
@@ -1420,8 +1435,8 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
   float* acc = f32 ? reinterpret_cast<float*>(y) : reinterpret_cast<float*>(ws + pl.off_acc);
   {
     LaunchTimer lt("ffn_f1_gather_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero};
-    const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero, 4};
+    const unsigned grid = (unsigned)route_grid(ra);
     if (dual)
       hipLaunchKernelGGL((f1_gather_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
                          eti, dm.d, dm.h, A, B, G);
@@ -1431,8 +1446,8 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_f2_down_combine", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero};
-    const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero, 1};
+    const unsigned grid = (unsigned)route_grid(ra);
     hipLaunchKernelGGL((f2_down_combine<T>), dim3(grid), dim3(NT), 0, s, ra, G, W2T, ls.list, eti,
                        gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc);
   }
@@ -1453,8 +1468,8 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   const int nNh = (int)cdiv(dm.h, 256);
   {
     LaunchTimer lt("ffn_b1_dgrad_glu", s);
-    RouteArgs ra{ls.tiles_route, pl.route_tiles, nNh, (const char*)ls.zero};
-    const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
+    RouteArgs ra{ls.tiles_route, pl.route_tiles, nNh, (const char*)ls.zero, 1};
+    const unsigned grid = (unsigned)route_grid(ra);
 #define MOE_B1(DU, RO)                                                                          \
   hipLaunchKernelGGL((b1_dgrad_glu<T, DU, RO>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti, gate_p, \
                      dm.d, dm.h, A, B, Gs, dgp)
@@ -1492,8 +1507,8 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_b3_dx", s);
-    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero};
-    const unsigned grid = (unsigned)round8(ra.ntiles * ra.nN);
+    RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero, 1};
+    const unsigned grid = (unsigned)route_grid(ra);
     if (dual)
       hipLaunchKernelGGL((b3_dx<T, true>), dim3(grid), dim3(NT), 0, s, ra, A, B, W1, W3, ls.list,
                          eti, dm.d, dm.h, pass_mode(dm.K, k, f32), dx, acc);
