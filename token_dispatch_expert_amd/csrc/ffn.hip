@@ -54,8 +54,7 @@ constexpr int TBM = 256;                 // output tile rows
 constexpr int TBN = 256;                 // output tile columns (logical)
 constexpr int ROWB = 128;                // bytes of k per LDS row per k-tile
 constexpr int OPB = 256 * ROWB;          // one operand tile in LDS (32 KB)
-constexpr int STAGE = 2 * OPB;           // A + B
-constexpr int LDSB = 2 * STAGE;          // double buffered (128 KB)
+constexpr int STAGE = 2 * OPB;           // A + B; two stages (128 KB)
 constexpr int MT = 4, NTL = 2;           // MFMA 32x32 tiles per wavefront (M, N)
 
 template <typename T> struct Traits;
@@ -111,7 +110,7 @@ template <typename T>
 struct KLoaderD {
   static constexpr bool kDirect = true;
   const char* rp[4];      // row start (absent row: nullptr)
-  int cj[4];              // logical chunk fetched in load j
+  int c0;                 // logical chunk fetched in load 0 (load j: c0 ^ j)
   const char* zero;       // 16 zero bytes
   int64_t delta;
   int ksplit, klen;
@@ -119,19 +118,18 @@ struct KLoaderD {
   __device__ static __forceinline__ int row_of(int j) {
     return (threadIdx.x >> 6) * 32 + 8 * j + ((threadIdx.x & 63) >> 3);
   }
+  // Row r = 32 w + 8 j + (l >> 3) has swizzle (r ^ (r >> 3)) & 7 =
+  // (l >> 3) ^ (4 (w & 1) + j) for j < 4, so load j fetches chunk c0 ^ j.
   __device__ __forceinline__ void init_chunks() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = row_of(j);
-      cj[j] = (threadIdx.x & 7) ^ ((r ^ (r >> 3)) & 7);
-    }
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    c0 = (l & 7) ^ (l >> 3) ^ ((w & 1) << 2);
   }
   __device__ __forceinline__ void issue(int kt, char* lds) const {
     constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = kt * KT + cj[j] * VEC;
+      const int k = kt * KT + (c0 ^ j) * VEC;
       const bool ok = rp[j] != nullptr && k < klen;
       const char* g = k < ksplit ? rp[j] + (int64_t)k * ES : rp[j] + delta + (int64_t)(k - ksplit) * ES;
       load_to_lds(ok ? g : zero, lds + (w * 32 + 8 * j) * ROWB);
@@ -272,7 +270,7 @@ struct TLoaderD {
   int64_t rbase;
   int klen;
   const char* zero;
-  int64_t rnext[4];
+  int32_t rnext[4];       // row indices of the next k-tile (as loaded)
 
   __device__ static __forceinline__ int krow(int j) {
     return (threadIdx.x >> 6) * 8 + 2 * j + ((threadIdx.x & 63) >> 5);
@@ -287,16 +285,19 @@ struct TLoaderD {
   __device__ __forceinline__ void setup(const char* b0, const char* b1, int first_pos, int limit,
                                         int64_t ld_, const int32_t* ridx_, int64_t rbase_,
                                         int klen_, const char* zero_);
-  __device__ __forceinline__ void rows_of(int kt, int64_t (&rr)[4]) const {
+  // The index array is never read past klen (a k-row past it reads entry 0
+  // and copies the zero page instead).  The loaded value is used only by the
+  // next k-tile's copies, so nothing waits for it here.
+  __device__ __forceinline__ void rows_of(int kt, int32_t (&rr)[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = kt * 64 + krow(j);
-      const bool in = k < klen;  // the index array is never read past klen
-      rr[j] = ridx != nullptr ? (in ? (int64_t)ridx[k] : 0) : rbase + (in ? k : 0);
+      const bool in = k < klen;
+      rr[j] = ridx != nullptr ? ridx[in ? k : 0] : (int32_t)rbase + (in ? k : 0);
     }
   }
   __device__ __forceinline__ void issue(int kt, char* lds) {
-    int64_t r[4];
+    int32_t r[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = rnext[j];
     rows_of(kt + 1, rnext);
@@ -426,10 +427,36 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
   }
 }
 
+// One k-tile: the next k-tile's copies into nxt go out first, then the
+// MFMAs on cur; everything lands before the barrier.
+template <typename T, class LA, class LB, bool TR>
+__device__ __forceinline__ void ktile_step(LA& la, LB& lb, int kt, int nk, char* cur, char* nxt,
+                                           Acc& acc, Frags& f) {
+  constexpr bool DA = LA::kDirect, DB = LB::kDirect;
+  const bool more = kt + 1 < nk;
+  if (more) {
+    if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
+    if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+  }
+  mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
+  if (more) {
+    if constexpr (!DA) la.store(nxt);
+    if constexpr (!DB) lb.store(nxt + OPB);
+  }
+  if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 // Main loop over nk k-tiles; result in acc (zero when nk == 0).  TR: both
-// operands are TLoaderD tiles read with the transposing LDS read.
+// operands are TLoaderD tiles read with the transposing LDS read.  The two
+// LDS stages are distinct arrays and the loop is unrolled by two, so every
+// access names its stage: the compiler can then see that fragment reads of
+// one stage do not overlap the direct-to-LDS copies into the other, and
+// does not wait for those copies before reading (with one array it must
+// assume they may overlap, which serialises copies and MFMAs).
 template <typename T, class LA, class LB, bool TR = false>
-__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
+__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* st0, char* st1,
+                                              Acc& acc) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -438,26 +465,14 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
       for (int i = 0; i < 16; ++i) acc.c[mt][nt][i] = 0.f;
   if (nk <= 0) return;
   constexpr bool DA = LA::kDirect, DB = LB::kDirect;
-  if constexpr (DA) la.issue(0, smem); else { la.fetch(0); la.store(smem); }
-  if constexpr (DB) lb.issue(0, smem + OPB); else { lb.fetch(0); lb.store(smem + OPB); }
+  if constexpr (DA) la.issue(0, st0); else { la.fetch(0); la.store(st0); }
+  if constexpr (DB) lb.issue(0, st0 + OPB); else { lb.fetch(0); lb.store(st0 + OPB); }
   if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frags f;
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
-      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
-    }
-    mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
-    if (more) {
-      if constexpr (!DA) la.store(nxt);
-      if constexpr (!DB) lb.store(nxt + OPB);
-    }
-    if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    ktile_step<T, LA, LB, TR>(la, lb, kt, nk, st0, st1, acc, f);
+    if (kt + 1 < nk) ktile_step<T, LA, LB, TR>(la, lb, kt + 1, nk, st1, st0, acc, f);
   }
   mma_chunk<T>(f.a[1], f.b[1], acc);
 }
@@ -771,7 +786,8 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
                                                        const int32_t* __restrict__ eti, int d,
                                                        int h, T* __restrict__ A,
                                                        T* __restrict__ B, T* __restrict__ G) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
   int ntile;
@@ -799,7 +815,7 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, st0, st1, acc);
 
   // tile-relative 32-bit offsets from the tile's first row (at most 256 rows)
   const int64_t tb = (int64_t)rb * h;
@@ -901,12 +917,12 @@ __device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t*
 
 // Called after the main loop's final barrier (LDS free, s_t / s_g visible).
 template <typename T, int MODE>
-__device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, const int32_t* s_t,
+__device__ __forceinline__ void combine_epilogue(const Acc& acc, char* st0, char* st1, const int32_t* s_t,
                                                  const float* s_g, int n0, int d,
                                                  T* __restrict__ out, float* __restrict__ accb) {
   const int w = threadIdx.x >> 6, cl = (threadIdx.x & 63) * 4;
   const int c = n0 + cl;
-  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + 64 * 256};
+  float* sb[2] = {reinterpret_cast<float*>(st0), reinterpret_cast<float*>(st1)};
   const int32_t* s_tw = s_t + w;
   const float* s_gw = s_g + w;
   float4 p[2][CCH];
@@ -925,14 +941,14 @@ __device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, con
 }
 
 template <typename T>
-__device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, const int32_t* s_t,
+__device__ __forceinline__ void combine_dispatch(const Acc& acc, char* st0, char* st1, const int32_t* s_t,
                                                  const float* s_g, int n0, int d, int mode,
                                                  T* __restrict__ out, float* __restrict__ accb) {
   switch (mode) {
-    case 0: combine_epilogue<T, 0>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    case 1: combine_epilogue<T, 1>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    case 2: combine_epilogue<T, 2>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    default: combine_epilogue<T, 3>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 0: combine_epilogue<T, 0>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
+    case 1: combine_epilogue<T, 1>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
+    case 2: combine_epilogue<T, 2>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
+    default: combine_epilogue<T, 3>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
   }
 }
 
@@ -947,7 +963,8 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
                                                          int k, int d, int h, int mode,
                                                          T* __restrict__ y,
                                                          float* __restrict__ yacc) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
@@ -977,9 +994,9 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   lb.delta = 0;
   lb.ksplit = lb.klen = h;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, st0, st1, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, y, yacc);
+  combine_dispatch<T>(acc, st0, st1, s_t, s_g, n0, d, mode, y, yacc);
 }
 
 // B1 epilogue on 8-column chunks: dG = gate * acc; with s = sigmoid(A),
@@ -990,14 +1007,14 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
 // of acc * SiLU(A) [* B]; a row's 32 chunk lanes are summed by a fixed
 // butterfly, so the value does not depend on timing.
 template <typename T, bool DUAL, bool ROUTER>
-__device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const float* s_g, int rb,
+__device__ __forceinline__ void b1_epilogue(const Acc& acc, char* st0, char* st1, const float* s_g, int rb,
                                             int re, int n0, int h, int nN, int ntile,
                                             T* __restrict__ A, T* __restrict__ B,
                                             T* __restrict__ Gs, float* __restrict__ dgp) {
   constexpr int CPT = 4;                    // chunks per thread per quarter (32 per row)
   constexpr bool PF = sizeof(T) == 2;       // prefetch the next quarter
   constexpr int NB = PF ? 2 : 1;
-  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + 64 * 256};
+  float* sb[2] = {reinterpret_cast<float*>(st0), reinterpret_cast<float*>(st1)};
   const int ch = threadIdx.x & 31, r0 = threadIdx.x >> 5;  // rows r0 + 16 j
   const int c = n0 + ch * 8;
   Raw8<T> xa[NB][CPT], xb[NB][CPT];
@@ -1081,7 +1098,8 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
                                                       int h, T* __restrict__ A,
                                                       T* __restrict__ B, T* __restrict__ Gs,
                                                       float* __restrict__ dgp) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
@@ -1103,10 +1121,10 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, st0, st1, acc);
   __syncthreads();
 
-  b1_epilogue<T, DUAL, ROUTER>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+  b1_epilogue<T, DUAL, ROUTER>(acc, st0, st1, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
 // Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
@@ -1180,7 +1198,8 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
                                                 const int32_t* __restrict__ eti,
                                                 const int32_t* __restrict__ offsets, int d, int h,
                                                 T* __restrict__ dW2) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
   int e, mi, ni;
   if (!weight_tile(wa, e, mi, ni)) return;
@@ -1194,12 +1213,12 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
                     o0, n_e, wa.zero);
     lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
                     0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
     lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
   }
 
   T* out = dW2 + (int64_t)e * h * d;
@@ -1227,7 +1246,8 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
                                                  const int32_t* __restrict__ offsets, int d,
                                                  int h, T* __restrict__ dW1,
                                                  T* __restrict__ dW3) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
   int e, mi, ni;
   if (!weight_tile(wa, e, mi, ni)) return;
@@ -1241,7 +1261,7 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
                     n_e, wa.zero);
     lb.setup<DUAL>(reinterpret_cast<const char*>(dA), reinterpret_cast<const char*>(dB), n0, h,
                    (int64_t)h * ES, nullptr, o0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
@@ -1252,7 +1272,7 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
     const int sc = DUAL ? dual_col(lc) : lc;
     lb.setup(reinterpret_cast<const char*>(src == 0 ? dA : dB), n0 + sc - lc, h,
              (int64_t)h * ES, nullptr, o0, n_e);
-    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
   }
 
   T* o1 = dW1 + (int64_t)e * d * h;
@@ -1290,7 +1310,8 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
                                                const int32_t* __restrict__ eti, int d, int h,
                                                int mode, T* __restrict__ dx,
                                                float* __restrict__ dxacc) {
-  __shared__ __attribute__((aligned(16))) char smem[LDSB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
   __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
@@ -1317,9 +1338,9 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
   lb.ksplit = h;
   lb.klen = klen;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, st0, st1, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, dx, dxacc);
+  combine_dispatch<T>(acc, st0, st1, s_t, s_g, n0, d, mode, dx, dxacc);
 }
 
 // ------------------------------------------------------------------ host
