@@ -28,6 +28,8 @@ SMALL = [
     (400, 128, 64, 4, 4, SILU, W.F32),        # K = E
     (1, 64, 64, 8, 2, SWIGLU, W.BF16),        # L = 1
     (2500, 256, 512, 16, 4, SWIGLU, W.BF16),
+    (1100, 520, 648, 8, 3, SWIGLU, W.BF16),   # several column tiles, 8-wide last ones, odd k-tiles
+    (600, 264, 392, 4, 2, SILU, W.F32),
 ]
 
 

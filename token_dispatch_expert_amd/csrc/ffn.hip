@@ -428,15 +428,22 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
 }
 
 // One k-tile: the next k-tile's copies into nxt go out first, then the
-// MFMAs on cur; everything lands before the barrier.
-template <typename T, class LA, class LB, bool TR>
+// MFMAs on cur; everything lands before the barrier.  BFIRST: B's copies go
+// out before A's (measured: the operand whose rows are gathered through an
+// index array does best issued last).
+template <typename T, class LA, class LB, bool TR, bool BFIRST>
 __device__ __forceinline__ void ktile_step(LA& la, LB& lb, int kt, int nk, char* cur, char* nxt,
                                            Acc& acc, Frags& f) {
   constexpr bool DA = LA::kDirect, DB = LB::kDirect;
   const bool more = kt + 1 < nk;
   if (more) {
+    if constexpr (BFIRST) {
+      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+    }
     if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
-    if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+    if constexpr (!BFIRST) {
+      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+    }
   }
   mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
   if (more) {
@@ -454,7 +461,7 @@ __device__ __forceinline__ void ktile_step(LA& la, LB& lb, int kt, int nk, char*
 // one stage do not overlap the direct-to-LDS copies into the other, and
 // does not wait for those copies before reading (with one array it must
 // assume they may overlap, which serialises copies and MFMAs).
-template <typename T, class LA, class LB, bool TR = false>
+template <typename T, class LA, class LB, bool TR = false, bool BFIRST = false>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* st0, char* st1,
                                               Acc& acc) {
 #pragma unroll
@@ -471,8 +478,8 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* st0,
   __syncthreads();
   Frags f;
   for (int kt = 0; kt < nk; kt += 2) {
-    ktile_step<T, LA, LB, TR>(la, lb, kt, nk, st0, st1, acc, f);
-    if (kt + 1 < nk) ktile_step<T, LA, LB, TR>(la, lb, kt + 1, nk, st1, st0, acc, f);
+    ktile_step<T, LA, LB, TR, BFIRST>(la, lb, kt, nk, st0, st1, acc, f);
+    if (kt + 1 < nk) ktile_step<T, LA, LB, TR, BFIRST>(la, lb, kt + 1, nk, st1, st0, acc, f);
   }
   mma_chunk<T>(f.a[1], f.b[1], acc);
 }
@@ -1261,7 +1268,8 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
                     n_e, wa.zero);
     lb.setup<DUAL>(reinterpret_cast<const char*>(dA), reinterpret_cast<const char*>(dB), n0, h,
                    (int64_t)h * ES, nullptr, o0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
+    // x rows are gathered: their copies go out last
+    gemm_mainloop<T, TLoaderD, TLoaderD, true, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
