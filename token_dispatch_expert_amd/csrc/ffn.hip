@@ -90,12 +90,23 @@ __device__ __forceinline__ uint4 sel16(bool ok, uint4 v) {
 
 // ------------------------------------------------------------------ loaders
 
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // 16 bytes per lane straight from global memory into LDS: lane i of the
-// wavefront lands at lds_base + 16 i (lds_base is wavefront-uniform).
+// wavefront lands at lds_base + 16 i (lds_base is wavefront-uniform; it goes
+// in M0, which no compiler-generated code in these kernels uses).  Written
+// as inline assembly so that the compiler does not track these copies.
+// Tracked, it must prove that a copy cannot write the LDS a fragment read is
+// about to read, or else wait for every copy in flight before the read; that
+// proof depends on how it happens to lower the stage addresses, and when it
+// fails the copies and the MFMAs run back to back.  Every wait for the
+// copies is explicit in the main loop.
 __device__ __forceinline__ void load_to_lds(const void* g, char* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m), "v"(g)
+               : "memory");
 }
 
 // 256 rows with k contiguous in memory, copied straight into LDS.  Element k
@@ -427,43 +438,15 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
   }
 }
 
-// One k-tile: the next k-tile's copies into nxt go out first, then the
-// MFMAs on cur; everything lands before the barrier.  BFIRST: B's copies go
-// out before A's (measured: the operand whose rows are gathered through an
-// index array does best issued last).
-template <typename T, class LA, class LB, bool TR, bool BFIRST>
-__device__ __forceinline__ void ktile_step(LA& la, LB& lb, int kt, int nk, char* cur, char* nxt,
-                                           Acc& acc, Frags& f) {
-  constexpr bool DA = LA::kDirect, DB = LB::kDirect;
-  const bool more = kt + 1 < nk;
-  if (more) {
-    if constexpr (BFIRST) {
-      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
-    }
-    if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
-    if constexpr (!BFIRST) {
-      if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
-    }
-  }
-  mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
-  if (more) {
-    if constexpr (!DA) la.store(nxt);
-    if constexpr (!DB) lb.store(nxt + OPB);
-  }
-  if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
-
 // Main loop over nk k-tiles; result in acc (zero when nk == 0).  TR: both
-// operands are TLoaderD tiles read with the transposing LDS read.  The two
-// LDS stages are distinct arrays and the loop is unrolled by two, so every
-// access names its stage: the compiler can then see that fragment reads of
-// one stage do not overlap the direct-to-LDS copies into the other, and
-// does not wait for those copies before reading (with one array it must
-// assume they may overlap, which serialises copies and MFMAs).
+// operands are TLoaderD tiles read with the transposing LDS read.  smem
+// holds two stages of [A | B] (128 KB).  Step kt sends out the copies of
+// k-tile kt + 1 into the other stage, runs the MFMAs on stage kt, and waits
+// for its copies before the barrier.  BFIRST: B's copies go out before A's
+// (measured: the operand whose rows are gathered through an index array does
+// best issued last).
 template <typename T, class LA, class LB, bool TR = false, bool BFIRST = false>
-__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* st0, char* st1,
-                                              Acc& acc) {
+__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -472,14 +455,31 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* st0,
       for (int i = 0; i < 16; ++i) acc.c[mt][nt][i] = 0.f;
   if (nk <= 0) return;
   constexpr bool DA = LA::kDirect, DB = LB::kDirect;
-  if constexpr (DA) la.issue(0, st0); else { la.fetch(0); la.store(st0); }
-  if constexpr (DB) lb.issue(0, st0 + OPB); else { lb.fetch(0); lb.store(st0 + OPB); }
+  if constexpr (DA) la.issue(0, smem); else { la.fetch(0); la.store(smem); }
+  if constexpr (DB) lb.issue(0, smem + OPB); else { lb.fetch(0); lb.store(smem + OPB); }
   if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frags f;
-  for (int kt = 0; kt < nk; kt += 2) {
-    ktile_step<T, LA, LB, TR, BFIRST>(la, lb, kt, nk, st0, st1, acc, f);
-    if (kt + 1 < nk) ktile_step<T, LA, LB, TR, BFIRST>(la, lb, kt + 1, nk, st1, st0, acc, f);
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * STAGE;
+    char* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      if constexpr (BFIRST) {
+        if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+      }
+      if constexpr (DA) la.issue(kt + 1, nxt); else la.fetch(kt + 1);
+      if constexpr (!BFIRST) {
+        if constexpr (DB) lb.issue(kt + 1, nxt + OPB); else lb.fetch(kt + 1);
+      }
+    }
+    mma_ktile<T, TR>(cur, cur + OPB, acc, f, kt > 0);
+    if (more) {
+      if constexpr (!DA) la.store(nxt);
+      if constexpr (!DB) lb.store(nxt + OPB);
+    }
+    if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   mma_chunk<T>(f.a[1], f.b[1], acc);
 }
@@ -793,8 +793,7 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
                                                        const int32_t* __restrict__ eti, int d,
                                                        int h, T* __restrict__ A,
                                                        T* __restrict__ B, T* __restrict__ G) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
   int ntile;
@@ -822,7 +821,7 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, st0, st1, acc);
+  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
 
   // tile-relative 32-bit offsets from the tile's first row (at most 256 rows)
   const int64_t tb = (int64_t)rb * h;
@@ -924,12 +923,12 @@ __device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t*
 
 // Called after the main loop's final barrier (LDS free, s_t / s_g visible).
 template <typename T, int MODE>
-__device__ __forceinline__ void combine_epilogue(const Acc& acc, char* st0, char* st1, const int32_t* s_t,
+__device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, const int32_t* s_t,
                                                  const float* s_g, int n0, int d,
                                                  T* __restrict__ out, float* __restrict__ accb) {
   const int w = threadIdx.x >> 6, cl = (threadIdx.x & 63) * 4;
   const int c = n0 + cl;
-  float* sb[2] = {reinterpret_cast<float*>(st0), reinterpret_cast<float*>(st1)};
+  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem + STAGE)};
   const int32_t* s_tw = s_t + w;
   const float* s_gw = s_g + w;
   float4 p[2][CCH];
@@ -948,14 +947,14 @@ __device__ __forceinline__ void combine_epilogue(const Acc& acc, char* st0, char
 }
 
 template <typename T>
-__device__ __forceinline__ void combine_dispatch(const Acc& acc, char* st0, char* st1, const int32_t* s_t,
+__device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, const int32_t* s_t,
                                                  const float* s_g, int n0, int d, int mode,
                                                  T* __restrict__ out, float* __restrict__ accb) {
   switch (mode) {
-    case 0: combine_epilogue<T, 0>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
-    case 1: combine_epilogue<T, 1>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
-    case 2: combine_epilogue<T, 2>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
-    default: combine_epilogue<T, 3>(acc, st0, st1, s_t, s_g, n0, d, out, accb); break;
+    case 0: combine_epilogue<T, 0>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 1: combine_epilogue<T, 1>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 2: combine_epilogue<T, 2>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    default: combine_epilogue<T, 3>(acc, smem, s_t, s_g, n0, d, out, accb); break;
   }
 }
 
@@ -970,8 +969,7 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
                                                          int k, int d, int h, int mode,
                                                          T* __restrict__ y,
                                                          float* __restrict__ yacc) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
@@ -1001,9 +999,9 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   lb.delta = 0;
   lb.ksplit = lb.klen = h;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, st0, st1, acc);
+  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, st0, st1, s_t, s_g, n0, d, mode, y, yacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, y, yacc);
 }
 
 // B1 epilogue on 8-column chunks: dG = gate * acc; with s = sigmoid(A),
@@ -1014,14 +1012,14 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
 // of acc * SiLU(A) [* B]; a row's 32 chunk lanes are summed by a fixed
 // butterfly, so the value does not depend on timing.
 template <typename T, bool DUAL, bool ROUTER>
-__device__ __forceinline__ void b1_epilogue(const Acc& acc, char* st0, char* st1, const float* s_g, int rb,
+__device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const float* s_g, int rb,
                                             int re, int n0, int h, int nN, int ntile,
                                             T* __restrict__ A, T* __restrict__ B,
                                             T* __restrict__ Gs, float* __restrict__ dgp) {
   constexpr int CPT = 4;                    // chunks per thread per quarter (32 per row)
   constexpr bool PF = sizeof(T) == 2;       // prefetch the next quarter
   constexpr int NB = PF ? 2 : 1;
-  float* sb[2] = {reinterpret_cast<float*>(st0), reinterpret_cast<float*>(st1)};
+  float* sb[2] = {reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem + STAGE)};
   const int ch = threadIdx.x & 31, r0 = threadIdx.x >> 5;  // rows r0 + 16 j
   const int c = n0 + ch * 8;
   Raw8<T> xa[NB][CPT], xb[NB][CPT];
@@ -1105,8 +1103,7 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
                                                       int h, T* __restrict__ A,
                                                       T* __restrict__ B, T* __restrict__ Gs,
                                                       float* __restrict__ dgp) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
   int4 ds;
@@ -1128,10 +1125,10 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, st0, st1, acc);
+  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
   __syncthreads();
 
-  b1_epilogue<T, DUAL, ROUTER>(acc, st0, st1, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+  b1_epilogue<T, DUAL, ROUTER>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
 // Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
@@ -1205,8 +1202,7 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
                                                 const int32_t* __restrict__ eti,
                                                 const int32_t* __restrict__ offsets, int d, int h,
                                                 T* __restrict__ dW2) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
   int e, mi, ni;
   if (!weight_tile(wa, e, mi, ni)) return;
@@ -1220,12 +1216,12 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
                     o0, n_e, wa.zero);
     lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
                     0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
     lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   }
 
   T* out = dW2 + (int64_t)e * h * d;
@@ -1253,8 +1249,7 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
                                                  const int32_t* __restrict__ offsets, int d,
                                                  int h, T* __restrict__ dW1,
                                                  T* __restrict__ dW3) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
   int e, mi, ni;
   if (!weight_tile(wa, e, mi, ni)) return;
@@ -1269,7 +1264,7 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
     lb.setup<DUAL>(reinterpret_cast<const char*>(dA), reinterpret_cast<const char*>(dB), n0, h,
                    (int64_t)h * ES, nullptr, o0, n_e, wa.zero);
     // x rows are gathered: their copies go out last
-    gemm_mainloop<T, TLoaderD, TLoaderD, true, true>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(x), m0, d, (int64_t)d * ES, eti + o0, 0, n_e);
@@ -1280,7 +1275,7 @@ __global__ __launch_bounds__(NT, 1) void b2_dw13(WeightArgs wa, const T* __restr
     const int sc = DUAL ? dual_col(lc) : lc;
     lb.setup(reinterpret_cast<const char*>(src == 0 ? dA : dB), n0 + sc - lc, h,
              (int64_t)h * ES, nullptr, o0, n_e);
-    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, st0, st1, acc);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   }
 
   T* o1 = dW1 + (int64_t)e * d * h;
@@ -1318,8 +1313,7 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
                                                const int32_t* __restrict__ eti, int d, int h,
                                                int mode, T* __restrict__ dx,
                                                float* __restrict__ dxacc) {
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
   constexpr int KT = Traits<T>::KT;
@@ -1346,9 +1340,9 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
   lb.ksplit = h;
   lb.klen = klen;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, st0, st1, acc);
+  gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, st0, st1, s_t, s_g, n0, d, mode, dx, dxacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, dx, dxacc);
 }
 
 // ------------------------------------------------------------------ host
