@@ -30,6 +30,7 @@ SMALL = [
     (2500, 256, 512, 16, 4, SWIGLU, W.BF16),
     (1100, 520, 648, 8, 3, SWIGLU, W.BF16),   # several column tiles, 8-wide last ones, odd k-tiles
     (600, 264, 392, 4, 2, SILU, W.F32),
+    (700, 2048, 384, 4, 2, SWIGLU, W.BF16),   # 8 dW1/dW3 row tiles: the M-fastest tile order
 ]
 
 
