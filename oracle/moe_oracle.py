@@ -36,7 +36,7 @@ not the three-step GPU construction.  The one place where the oracle keeps an
 (L*K, d) per-route buffer is deliberate: it is the conventional formulation
 the method is measured against.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 * W1 is the gate projection, W3 the up projection (SwiGLU only), W2 the down
   projection; layouts W1, W3: [E, d, h], W2: [E, h, d]; no biases.
 * Top-K ties at the K-th place go to the lower expert id.

@@ -63,8 +63,8 @@ def load_library(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise OSError(f"{path} is not built; run __graft_entry__.build() "
-                      "or python token_dispatch_expert_amd/build_lib.py")
+        raise OSError(f"{path} is not built; run "
+                      "python token_dispatch_expert_amd/build_lib.py")
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     SZ = ctypes.POINTER(ctypes.c_size_t)
