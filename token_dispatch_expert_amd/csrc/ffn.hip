@@ -823,40 +823,63 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
   Acc acc;
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
 
-  // tile-relative 32-bit offsets from the tile's first row (at most 256 rows)
+  // Stores address a scalar tile base plus a 32-bit byte offset.  A lane's
+  // column and its row inside each group of four are fixed; the rest of the
+  // row is uniform, so each row adds one scalar term to a fixed lane offset.
+  // Full tiles (every tile of an expert segment but its last) skip the row
+  // bound check.
   const int64_t tb = (int64_t)rb * h;
   T* At = A + tb;
   T* Bt = DUAL ? B + tb : nullptr;
   T* Gt = G + tb;
+  const int lane = threadIdx.x & 63;
+  const int wm = __builtin_amdgcn_readfirstlane(wave_m());
+  const int nrows = re - rb;
+  const int lrow = (lane >> 5) * 4;
+  auto store_rows = [&](auto check) {
+    constexpr bool CHECK = decltype(check)::value;
+    if (DUAL) {
+      const int c = n0 + dual_col(acc_col(0));
+      if (c >= h) return;
+      const uint32_t vo = (uint32_t)(lrow * h + c) * (uint32_t)sizeof(T);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = acc_row(mt, i);
-      if (rb + r >= re) continue;
-      if (DUAL) {
-        const int c = n0 + dual_col(acc_col(0));
-        if (c < h) {
+        for (int i = 0; i < 16; ++i) {
+          const int ru = wm * 128 + mt * 32 + (i >> 2) * 8 + (i & 3);  // uniform
+          if (CHECK && ru + lrow >= nrows) continue;
+          const uint32_t o = vo + (uint32_t)(ru * h) * (uint32_t)sizeof(T);
           const float a = acc.c[mt][0][i], b = acc.c[mt][1][i];
-          const uint32_t o = (uint32_t)(r * h + c) * (uint32_t)sizeof(T);  // bytes
           Elem<T>::store(byte_off(At, o), a);
           Elem<T>::store(byte_off(Bt, o), b);
           Elem<T>::store(byte_off(Gt, o), silu_of<T>(a) * b);
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) {
-          const int c = n0 + acc_col(nt);
-          if (c < h) {
+      for (int nt = 0; nt < NTL; ++nt) {
+        const int c = n0 + acc_col(nt);
+        if (c >= h) continue;
+        const uint32_t vo = (uint32_t)(lrow * h + c) * (uint32_t)sizeof(T);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ru = wm * 128 + mt * 32 + (i >> 2) * 8 + (i & 3);
+            if (CHECK && ru + lrow >= nrows) continue;
+            const uint32_t o = vo + (uint32_t)(ru * h) * (uint32_t)sizeof(T);
             const float a = acc.c[mt][nt][i];
-            const uint32_t o = (uint32_t)(r * h + c) * (uint32_t)sizeof(T);  // bytes
             Elem<T>::store(byte_off(At, o), a);
             Elem<T>::store(byte_off(Gt, o), silu_of<T>(a));
           }
         }
       }
     }
-  }
+  };
+  if (nrows >= 256)
+    store_rows(std::false_type{});
+  else
+    store_rows(std::true_type{});
 }
 
 // Slot-pass epilogue: out/acc row t = s_t[row] (-1: no row), scale s_g[row].
@@ -879,14 +902,14 @@ constexpr int CCH = 8;  // chunks per thread per quarter: 64 rows x 64 chunks / 
 // offset from one base.
 __device__ __forceinline__ constexpr int cq(int j) { return (j >> 2) * 128 + (j & 3) * 8; }
 
-template <int MODE>
+template <int MODE, bool FULL>
 __device__ __forceinline__ void combine_load(const int32_t* s_tw, int qq, int c, int d,
                                              const float* __restrict__ accb, float4 prev[CCH]) {
   if constexpr (MODE >= 2) {
 #pragma unroll
     for (int j = 0; j < CCH; ++j) {
       const int t = s_tw[cq(j) + 32 * qq];
-      const bool ok = t >= 0 && c < d;
+      const bool ok = FULL || (t >= 0 && c < d);
       // absent chunks read the (valid) first chunk and are never used
       const int64_t o = (int64_t)(ok ? t : 0) * d + (ok ? c : 0);
       prev[j] = *reinterpret_cast<const float4*>(accb + o);
@@ -894,7 +917,7 @@ __device__ __forceinline__ void combine_load(const int32_t* s_tw, int qq, int c,
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool FULL>
 __device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t* s_tw,
                                                 const float* s_gw, int qq, int c, int d,
                                                 const float4 prev[CCH], T* __restrict__ out,
@@ -902,7 +925,7 @@ __device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t*
 #pragma unroll
   for (int j = 0; j < CCH; ++j) {
     const int t = s_tw[cq(j) + 32 * qq];
-    if (t < 0 || c >= d) continue;
+    if (!FULL && (t < 0 || c >= d)) continue;
     const float g = s_gw[cq(j) + 32 * qq];
     const float4 a = *reinterpret_cast<const float4*>(sbw + j * 8 * 256);
     float4 v = make_float4(g * a.x, g * a.y, g * a.z, g * a.w);
@@ -922,7 +945,11 @@ __device__ __forceinline__ void combine_quarter(const float* sbw, const int32_t*
 }
 
 // Called after the main loop's final barrier (LDS free, s_t / s_g visible).
-template <typename T, int MODE>
+// FULL: every row of the tile is present and every column is inside d, so
+// no store is conditional.  (The compiler cannot count a store that a branch
+// may skip; with such stores between the accumulator loads, its waits for
+// the later loads also wait for earlier stores to complete.)
+template <typename T, int MODE, bool FULL>
 __device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, const int32_t* s_t,
                                                  const float* s_g, int n0, int d,
                                                  T* __restrict__ out, float* __restrict__ accb) {
@@ -932,30 +959,44 @@ __device__ __forceinline__ void combine_epilogue(const Acc& acc, char* smem, con
   const int32_t* s_tw = s_t + w;
   const float* s_gw = s_g + w;
   float4 p[2][CCH];
-  combine_load<MODE>(s_tw, 0, c, d, accb, p[0]);
+  combine_load<MODE, FULL>(s_tw, 0, c, d, accb, p[0]);
   park_quarter(acc, sb[0], 0);
-  combine_load<MODE>(s_tw, 1, c, d, accb, p[1]);
+  combine_load<MODE, FULL>(s_tw, 1, c, d, accb, p[1]);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < MT; ++q) {
     // buffer (q + 1) & 1 was last read before the previous barrier
     if (q + 1 < MT) park_quarter(acc, sb[(q + 1) & 1], q + 1);
-    combine_quarter<T, MODE>(sb[q & 1] + w * 256 + cl, s_tw, s_gw, q, c, d, p[q & 1], out, accb);
-    if (q + 2 < MT) combine_load<MODE>(s_tw, q + 2, c, d, accb, p[q & 1]);
+    combine_quarter<T, MODE, FULL>(sb[q & 1] + w * 256 + cl, s_tw, s_gw, q, c, d, p[q & 1], out,
+                                   accb);
+    if (q + 2 < MT) combine_load<MODE, FULL>(s_tw, q + 2, c, d, accb, p[q & 1]);
     if (q + 1 < MT) __syncthreads();
   }
 }
 
+template <typename T, bool FULL>
+__device__ __forceinline__ void combine_modes(const Acc& acc, char* smem, const int32_t* s_t,
+                                              const float* s_g, int n0, int d, int mode,
+                                              T* __restrict__ out, float* __restrict__ accb) {
+  switch (mode) {
+    case 0: combine_epilogue<T, 0, FULL>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 1: combine_epilogue<T, 1, FULL>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    case 2: combine_epilogue<T, 2, FULL>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+    default: combine_epilogue<T, 3, FULL>(acc, smem, s_t, s_g, n0, d, out, accb); break;
+  }
+}
+
+// nrows: rows present in the tile (the rest of s_t is -1).
 template <typename T>
 __device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, const int32_t* s_t,
-                                                 const float* s_g, int n0, int d, int mode,
-                                                 T* __restrict__ out, float* __restrict__ accb) {
-  switch (mode) {
-    case 0: combine_epilogue<T, 0>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    case 1: combine_epilogue<T, 1>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    case 2: combine_epilogue<T, 2>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-    default: combine_epilogue<T, 3>(acc, smem, s_t, s_g, n0, d, out, accb); break;
-  }
+                                                 const float* s_g, int nrows, int n0, int d,
+                                                 int mode, T* __restrict__ out,
+                                                 float* __restrict__ accb) {
+  // uniform across the workgroup; made scalar so the choice is one branch
+  if (__builtin_amdgcn_readfirstlane((nrows == TBM && n0 + 256 <= d) ? 1 : 0))
+    combine_modes<T, true>(acc, smem, s_t, s_g, n0, d, mode, out, accb);
+  else
+    combine_modes<T, false>(acc, smem, s_t, s_g, n0, d, mode, out, accb);
 }
 
 // F2 (slot pass k): O = G W2_e for the pass's rows, y[t] (+)= gate * O.
@@ -1001,7 +1042,7 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   Acc acc;
   gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, y, yacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, re - rb, n0, d, mode, y, yacc);
 }
 
 // B1 epilogue on 8-column chunks: dG = gate * acc; with s = sigmoid(A),
@@ -1010,8 +1051,10 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
 // bf16: the checkpoint loads of quarter q + 1 are in flight while quarter q
 // is processed.  ROUTER: dgp[p * nN + ntile] = sum over the tile's columns
 // of acc * SiLU(A) [* B]; a row's 32 chunk lanes are summed by a fixed
-// butterfly, so the value does not depend on timing.
-template <typename T, bool DUAL, bool ROUTER>
+// butterfly, so the value does not depend on timing.  FULL: all rows present
+// and all columns inside h, so no store sits under a branch (see
+// combine_epilogue for why that matters to the waits on the loads).
+template <typename T, bool DUAL, bool ROUTER, bool FULL>
 __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const float* s_g, int rb,
                                             int re, int n0, int h, int nN, int ntile,
                                             T* __restrict__ A, T* __restrict__ B,
@@ -1027,7 +1070,7 @@ __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const fl
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int p = rb + quarter_row(q, r0 + 16 * j);
-      const bool ok = p < re && c < h;
+      const bool ok = FULL || (p < re && c < h);
       // absent chunks read the (valid) first chunk and are never used
       const int64_t o = ok ? (int64_t)p * h + c : 0;
       xa[buf][j].load(A + o);
@@ -1051,7 +1094,7 @@ __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const fl
       const int row = quarter_row(q, r);
       const int p = rb + row;
       float rdot = 0.f;
-      if (p < re && c < h) {
+      if (FULL || (p < re && c < h)) {
         const int64_t o = (int64_t)p * h + c;
         const float gp = s_g[row];
         float v[8], a[8], b[8], da[8], db[8], gs[8];
@@ -1128,7 +1171,10 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
   __syncthreads();
 
-  b1_epilogue<T, DUAL, ROUTER>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+  if (__builtin_amdgcn_readfirstlane((re - rb == TBM && n0 + 256 <= h) ? 1 : 0))
+    b1_epilogue<T, DUAL, ROUTER, true>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+  else
+    b1_epilogue<T, DUAL, ROUTER, false>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
 // Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
@@ -1342,7 +1388,7 @@ __global__ __launch_bounds__(NT, 1) void b3_dx(RouteArgs ra, const T* __restrict
   Acc acc;
   gemm_mainloop<T>(la, lb, (klen + KT - 1) / KT, smem, acc);
   __syncthreads();
-  combine_dispatch<T>(acc, smem, s_t, s_g, n0, d, mode, dx, dxacc);
+  combine_dispatch<T>(acc, smem, s_t, s_g, re - rb, n0, d, mode, dx, dxacc);
 }
 
 // ------------------------------------------------------------------ host
