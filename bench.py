@@ -79,6 +79,16 @@ def dispatch_bytes(cfg):
     return b
 
 
+def dispatch_bytes_byte_map(cfg):
+    """Bytes of one dispatch build in the method's own layout with a one-byte
+    token-expert map entry: logits read (4LE), the map written once and read
+    twice (count, then scan and scatter: 3LE), the four L*K outputs (16LK) and
+    the offsets.  Reported beside the implemented layout's figure, which
+    moves fewer bytes for E <= 64 (bit masks)."""
+    L, E, K = cfg.L, cfg.E, cfg.K
+    return 4 * L * E + 3 * L * E + 16 * L * K + 4 * (E + 1)
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "token_dispatch_expert_amd", "csrc"))):
@@ -432,7 +442,11 @@ def main():
         "roofline_dispatch": {"bound": "hbm", "achieved": disp_gbs, "peak": PEAK_HBM_GBS,
                               "unit": "GB/s",
                               "frac": (disp_gbs / PEAK_HBM_GBS) if disp_gbs else None,
-                              "bytes_per_build": dispatch_bytes(cfg), "ms_per_build": disp_ms},
+                              "bytes_per_build": dispatch_bytes(cfg), "ms_per_build": disp_ms,
+                              "byte_map_model": {
+                                  "bytes_per_build": dispatch_bytes_byte_map(cfg),
+                                  "frac": (dispatch_bytes_byte_map(cfg) / (disp_ms / 1e3) / 1e9
+                                           / PEAK_HBM_GBS) if disp_ms > 0 else None}},
         "assignments_per_s": cfg.R / (ms_step / 1e3),
         "gemm_tflops_all": total_flops / (gemm_ms / 1e3) / 1e12,
         "kernels": per_kernel,

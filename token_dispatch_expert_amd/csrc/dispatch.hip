@@ -739,12 +739,12 @@ __global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt,
     __syncthreads();
     const int wv = s_w[lane];
     const int wex = wave_incl_scan(wv, lane) - wv;  // before (round, wave) = lane
-    const int ptot = __shfl(wex + wv, 63);
+    const int ptot = __builtin_amdgcn_readlane(wex + wv, 63);
     const int64_t add = r * row_offset + run;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int c = c0 + j * 256 + threadIdx.x;
-      const int before = __shfl(wex, j * 4 + wave);
+      const int before = __builtin_amdgcn_readlane(wex, j * 4 + wave);  // wave-uniform lane
       if (c < C) out[c] = (int32_t)(add + before + ex[j]);
     }
     run += ptot;

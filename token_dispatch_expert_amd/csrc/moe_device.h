@@ -46,13 +46,19 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// Wave-wide inclusive prefix sum.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
+// Wave-wide inclusive prefix sum; every lane of the wave must be active.
+// Data-parallel-primitive moves only (no LDS round trips): shifts by 1, 2, 4
+// and 8 inside each row of 16 lanes give the row scans, then the last lane
+// of row 0 is added to row 1 and of row 2 to row 3 (row_bcast:15), and the
+// last lane of row 1 to rows 2 and 3 (row_bcast:31).  Lanes without a source
+// add 0 (the `old` operand).
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
