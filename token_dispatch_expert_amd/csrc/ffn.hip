@@ -374,8 +374,16 @@ struct Acc {
   f32x16_t c[MT][NTL];
 };
 
+// Wavefront w of the eight owns the 128 x 64 block (wave_m, wave_n) of the
+// tile.  Wavefronts w and w + 4, which share a SIMD, differ in both their row
+// half and their column half (w + 4 takes the other column half), so a tile
+// whose last 128 rows or last 128 columns are padding still gives every SIMD
+// one wavefront of MFMA work.
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) >> 2; }
-__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) & 3; }
+__device__ __forceinline__ int wave_n() {
+  const int w = threadIdx.x >> 6;
+  return (w & 3) ^ ((w >> 2) << 1);
+}
 
 // MFMA fragments of two k-chunks (16 k each).  A k-tile's last chunk stays
 // in slot 1 past the barrier that ends the tile: its MFMAs issue at the start
@@ -445,8 +453,13 @@ __device__ __forceinline__ void mma_ktile(const char* As, const char* Bs, Acc& a
 // for its copies before the barrier.  BFIRST: B's copies go out before A's
 // (measured: the operand whose rows are gathered through an index array does
 // best issued last).
-template <typename T, class LA, class LB, bool TR = false, bool BFIRST = false>
-__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc) {
+// SKIP: `live` is false for a wavefront whose whole block lies in the
+// padding of the tile; that wavefront runs a loop of its own that copies its
+// share of the operands and meets every barrier, but reads no fragments and
+// issues no MFMAs (its accumulators stay zero).
+template <typename T, class LA, class LB, bool TR = false, bool BFIRST = false, bool SKIP = false>
+__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, Acc& acc,
+                                              bool live = true) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -455,6 +468,25 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
       for (int i = 0; i < 16; ++i) acc.c[mt][nt][i] = 0.f;
   if (nk <= 0) return;
   constexpr bool DA = LA::kDirect, DB = LB::kDirect;
+  if constexpr (SKIP) {
+    static_assert(DA && DB, "copies-only loop for direct-to-LDS operands");
+    if (__builtin_amdgcn_readfirstlane(live ? 1 : 0) == 0) {  // wave-uniform
+      la.issue(0, smem);
+      lb.issue(0, smem + OPB);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        char* nxt = smem + ((kt + 1) & 1) * STAGE;
+        if constexpr (BFIRST) lb.issue(kt + 1, nxt + OPB);
+        la.issue(kt + 1, nxt);
+        if constexpr (!BFIRST) lb.issue(kt + 1, nxt + OPB);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      __syncthreads();  // the live loop's last barrier
+      return;
+    }
+  }
   if constexpr (DA) la.issue(0, smem); else { la.fetch(0); la.store(smem); }
   if constexpr (DB) lb.issue(0, smem + OPB); else { lb.fetch(0); lb.store(smem + OPB); }
   if constexpr (DA || DB) __builtin_amdgcn_s_waitcnt(0);
@@ -1167,8 +1199,11 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   kloaderd_rows<T>(lb, W2 + (int64_t)e * h * d, nullptr, nullptr, n0, h, d, ra.zero);
   lb.delta = 0;
   lb.ksplit = lb.klen = d;
+  // with h % 256 == 128 the last column tile's second column half is padding
+  const bool live = n0 + wave_n() * 64 < h && rb + wave_m() * 128 < re;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (d + KT - 1) / KT, smem, acc);
+  gemm_mainloop<T, KLoaderD<T>, KLoaderD<T>, false, false, true>(la, lb, (d + KT - 1) / KT, smem,
+                                                                   acc, live);
   __syncthreads();
 
   if (__builtin_amdgcn_readfirstlane((re - rb == TBM && n0 + 256 <= h) ? 1 : 0))
@@ -1254,6 +1289,8 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
   if (!weight_tile(wa, e, mi, ni)) return;
   const int m0 = mi * 256, n0 = ni * 256;
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
+  // with h % 256 == 128 the last M tile's second row half is padding
+  const bool live = m0 + wave_m() * 128 < h && n0 + wave_n() * 64 < d;
 
   Acc acc;
   if constexpr (std::is_same<T, bf16_t>::value) {
@@ -1262,7 +1299,8 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
                     o0, n_e, wa.zero);
     lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
                     0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true, false, true>(la, lb, (n_e + KT - 1) / KT, smem, acc,
+                                                            live);
   } else {
     MNLoader<T> la, lb;
     la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
