@@ -1,0 +1,60 @@
+"""CPU checks on the algorithmic work bench.py divides by (the numerators of
+its roofline figures), against closed forms for the layer:
+
+* forward + backward of one layer is 18 d h flops per route for SwiGLU
+  (six products of 2 d h per route: first layer twice, second layer, dG, dW2,
+  dW1/dW3 twice, dx twice) and 12 d h for SiLU;
+* one dispatch build in the method's byte-map layout moves 4LE (logits) +
+  3LE (map written once, read twice) + 16LK (the four L*K outputs) + 4(E+1)
+  bytes: 544 bytes per token at L = 1M, E = 64, K = 6;
+* the bit-mask layout replaces the 3LE map bytes by 16L (token masks) and
+  the per-part columns, counts and tile bases.
+"""
+
+import bench
+from token_dispatch_expert_amd import workloads as W
+
+
+def _step_flops(cfg, kf):
+    per_launch = dict(kf)
+    launches = {k: 1 for k in kf}
+    launches["ffn_f2_down_combine"] = cfg.K   # slot passes
+    launches["ffn_b3_dx"] = cfg.K
+    return sum(per_launch[k] * launches[k] for k in kf)
+
+
+def test_step_flops_closed_form():
+    for ci in (1, 2, 3, 4, 5):
+        cfg = W.CONFIGS[ci]
+        per_route = (18 if cfg.act == W.SWIGLU else 12) * cfg.d * cfg.h
+        assert _step_flops(cfg, bench.kernel_flops(cfg)) == per_route * cfg.R
+
+
+def test_largest_config_flops():
+    cfg = W.CONFIGS[5]
+    kf = bench.kernel_flops(cfg)
+    assert kf["ffn_f1_gather_glu"] == 2 * 2 * 6_291_456 * 2048 * 1408       # 72.6 TFLOP
+    assert abs(_step_flops(cfg, kf) / 1e12 - 326.55) < 0.01
+    # config 2 (SiLU): 1,649 GFLOP per step
+    assert abs(_step_flops(W.CONFIGS[2], bench.kernel_flops(W.CONFIGS[2])) / 1e9 - 1649.3) < 0.1
+
+
+def test_dispatch_bytes_byte_map():
+    cfg = W.CONFIGS[5]
+    b = bench.dispatch_bytes_byte_map(cfg)
+    assert b == 570_425_604
+    assert round((b - 4 * (cfg.E + 1)) / cfg.L) == 544
+
+
+def test_dispatch_bytes_bit_mask():
+    cfg = W.CONFIGS[5]
+    L, E, K = cfg.L, cfg.E, cfg.K
+    tiles, parts = L // 256, L // 64
+    expect = (4 * L * E + 16 * L * K + 4 * (E + 1)      # logits, outputs, offsets
+              + 2 * 8 * L                              # token masks written and read
+              + 2 * 8 * E * parts                      # per-part columns
+              + 2 * 4 * E * parts + 2 * 4 * E * tiles)  # part counts, tile bases
+    assert bench.dispatch_bytes(cfg) == expect == 413_139_204
+    # byte-map configurations (E > 64) count the map as 2LE (written, read)
+    big = W.small_config(4096, 64, 64, 128, 6, W.SWIGLU, W.BF16)
+    assert bench.dispatch_bytes(big) == 4 * 4096 * 128 + 16 * 4096 * 6 + 4 * 129 + 2 * 4096 * 128
