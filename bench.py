@@ -447,6 +447,11 @@ def main():
                                   "bytes_per_build": dispatch_bytes_byte_map(cfg),
                                   "frac": (dispatch_bytes_byte_map(cfg) / (disp_ms / 1e3) / 1e9
                                            / PEAK_HBM_GBS) if disp_ms > 0 else None}},
+        "roofline_by_kernel": {
+            k: {"bound": "mfma", "achieved": v["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": v["tflops"] / peak, "traffic": measured_traffic(k, cfg.name),
+                "flops_per_launch": kflops[k], "avg_launch_ms": v["avg_launch_ms"]}
+            for k, v in gemm.items()},
         "assignments_per_s": cfg.R / (ms_step / 1e3),
         "gemm_tflops_all": total_flops / (gemm_ms / 1e3) / 1e12,
         "kernels": per_kernel,
