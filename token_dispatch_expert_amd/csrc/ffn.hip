@@ -573,23 +573,70 @@ __device__ __forceinline__ float sigm_of<float>(float a) { return 1.0f / (1.0f +
 
 // ------------------------------------------------------------------ weights
 
-// WT[e][c][r] = W[e][r][c] for an [E][R][C] tensor (64 x 64 tiles via LDS).
+// 16 bytes of a weight row as float32 (8 bf16 or 4 float32) and back.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
+    uint32_t q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      q[k] = (uint32_t)f2bf(v[2 * k]) | ((uint32_t)f2bf(v[2 * k + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void load(const float* p, float (&v)[8]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  __device__ static __forceinline__ void store(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// WT[e][c][r] = W[e][r][c] for an [E][R][C] tensor, 64 x 64 tiles through
+// LDS, 16 bytes per global load and store (R and C are multiples of 8 and
+// the tensors 16-byte aligned, so a 16-byte chunk never crosses a row end).
+// A bf16 value passes through float32 and back unchanged.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_weights(const T* __restrict__ W,
                                                          T* __restrict__ WT, int R, int C) {
+  constexpr int V = Vec16<T>::N;  // elements per chunk
+  constexpr int CPR = 64 / V;     // chunks per 64-element tile row
   __shared__ float tile[64][65];
   const int e = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const T* src = W + (int64_t)e * R * C;
   T* dst = WT + (int64_t)e * R * C;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, c = i & 63;
-    if (r0 + r < R && c0 + c < C) tile[r][c] = Elem<T>::load(src + (int64_t)(r0 + r) * C + c0 + c);
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, c = (i % CPR) * V;
+    if (r0 + r < R && c0 + c < C) {
+      float v[8];
+      Vec16<T>::load(src + (int64_t)(r0 + r) * C + c0 + c, v);
+#pragma unroll
+      for (int u = 0; u < V; ++u) tile[r][c + u] = v[u];
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int c = i >> 6, r = i & 63;
-    if (r0 + r < R && c0 + c < C) Elem<T>::store(dst + (int64_t)(c0 + c) * R + r0 + r, tile[r][c]);
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int c = i / CPR, r = (i % CPR) * V;
+    if (c0 + c < C && r0 + r < R) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < V; ++u) v[u] = tile[r + u][c];
+      Vec16<T>::store(dst + (int64_t)(c0 + c) * R + r0 + r, v);
+    }
   }
 }
 
