@@ -31,6 +31,9 @@ SMALL = [
     (1100, 520, 648, 8, 3, SWIGLU, W.BF16),   # several column tiles, 8-wide last ones, odd k-tiles
     (600, 264, 392, 4, 2, SILU, W.F32),
     (700, 2048, 384, 4, 2, SWIGLU, W.BF16),   # 8 dW1/dW3 row tiles: the M-fastest tile order
+    (600, 64, 128, 128, 4, SWIGLU, W.BF16),   # E = 128: byte-map dispatch, ~19 routes per expert
+    (500, 64, 64, 256, 8, SILU, W.F32),       # E = 256, K = 8: most experts hold one partial tile
+    (300, 64, 128, 32, 12, SWIGLU, W.BF16),   # K = 12 > 8: byte-map router, twelve slot passes
 ]
 
 
