@@ -34,6 +34,8 @@ SMALL = [
     (600, 64, 128, 128, 4, SWIGLU, W.BF16),   # E = 128: byte-map dispatch, ~19 routes per expert
     (500, 64, 64, 256, 8, SILU, W.F32),       # E = 256, K = 8: most experts hold one partial tile
     (300, 64, 128, 32, 12, SWIGLU, W.BF16),   # K = 12 > 8: byte-map router, twelve slot passes
+    (100, 64, 64, 256, 1, SWIGLU, W.BF16),    # K = 1, E = 256: most experts empty (dW exactly 0)
+    (64, 8, 8, 4, 2, SWIGLU, W.BF16),         # d = h = 8: one 16-byte chunk per row
 ]
 
 
