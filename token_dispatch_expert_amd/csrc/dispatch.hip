@@ -716,20 +716,22 @@ __global__ __launch_bounds__(256) void seg_scan(const int32_t* __restrict__ cnt,
   int32_t* out = base + (int64_t)r * C;
   int run = 0;
   for (int c0 = 0; c0 < C; c0 += 256 * V) {
+    // Every load goes out before any is used: entries past C read entry
+    // C - 1 (a branch around each load would make each wait for the last).
     int x[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int c = c0 + j * 256 + threadIdx.x;
-      x[j] = 0;
-      if (c < C) {
-        if constexpr (G == 4) {
-          const int4 q = *reinterpret_cast<const int4*>(in + (int64_t)c * 4);
-          x[j] = q.x + q.y + q.z + q.w;
-        } else {
+      const int64_t cc = c < C ? c : C - 1;
+      int v = 0;
+      if constexpr (G == 4) {
+        const int4 q = *reinterpret_cast<const int4*>(in + cc * 4);
+        v = q.x + q.y + q.z + q.w;
+      } else {
 #pragma unroll
-          for (int g = 0; g < G; ++g) x[j] += in[(int64_t)c * G + g];
-        }
+        for (int g = 0; g < G; ++g) v += in[cc * G + g];
       }
+      x[j] = c < C ? v : 0;
     }
     int ex[V];
 #pragma unroll
