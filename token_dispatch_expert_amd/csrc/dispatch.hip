@@ -683,16 +683,31 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
     }
   }
   __syncthreads();
+  // The staged values are read (indices clamped into the arrays) before any
+  // store goes out, so the LDS reads do not wait on each other behind the
+  // stores' bounds branches.
+  constexpr int NJ = MAXE / 256;
   const int n = min(s_run[64], MAXE);
   const int64_t R = L * K;
-  for (int j = tid; j < n; j += 256) {
-    const int pos = s_pos[j];
-    if (pos < R) eti[pos] = s_tok[j];  // always true when the masks hold K bits each
+  int pv[NJ], tv[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) {
+    const int j = min(tid + u * 256, MAXE - 1);
+    pv[u] = s_pos[j];
+    tv[u] = s_tok[j];
   }
+#pragma unroll
+  for (int u = 0; u < NJ; ++u)  // pos < R always holds when the masks hold K bits each
+    if (tid + u * 256 < n && pv[u] < R) eti[pv[u]] = tv[u];
   // rows t0 .. t0 + 255 of token_index_map are one contiguous run
   const int64_t t0 = (int64_t)tile * 256;
   const int nt = (int)min((int64_t)256, L - t0) * K;
-  for (int j = tid; j < nt; j += 256) tim[t0 * K + j] = s_tim[j];
+  int mv[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) mv[u] = s_tim[min(tid + u * 256, MAXE - 1)];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u)
+    if (tid + u * 256 < nt) tim[t0 * K + tid + u * 256] = mv[u];
 }
 
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
