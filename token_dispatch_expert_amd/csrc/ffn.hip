@@ -1259,11 +1259,13 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
     b1_epilogue<T, DUAL, ROUTER, false>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
-// Router gradient, one workgroup per 64 tokens.  Lane t of wavefront 0 adds
-// its token's route partials into dg_k = <dy[t], O[tim[t, k]]> (partials in
-// ascending tile order), forms the softmax backward over the selected logits
-// dz_k = g_k (dg_k - sum_j g_j dg_j) and parks the row in LDS; then the
-// workgroup writes the 64 full rows of dlogits (zeros for experts not chosen).
+// Router gradient, one workgroup per 64 tokens.  Every thread first takes
+// routes (t, k) of the block: dg_k = <dy[t], O[tim[t, k]]> is the sum of the
+// route's partials in ascending tile order, parked at the token's row in LDS
+// under its expert.  Then lane t of wavefront 0 forms the softmax backward
+// over the selected logits, dz_k = g_k (dg_k - sum_j g_j dg_j), sum in
+// ascending k, in place; then the workgroup writes the 64 full rows of
+// dlogits (zeros for experts not chosen).
 __global__ __launch_bounds__(256) void router_grad(const int32_t* __restrict__ tei,
                                                    const int32_t* __restrict__ tim,
                                                    const float* __restrict__ gates,
@@ -1275,23 +1277,32 @@ __global__ __launch_bounds__(256) void router_grad(const int32_t* __restrict__ t
   const int nrow = (int)min<int64_t>(64, L - t0);
   for (int i = threadIdx.x; i < nrow * E; i += 256) s_rows[i] = 0.f;
   __syncthreads();
+  const int nr = nrow * K;  // routes of the block: rows t0 .. t0 + nrow of tim, tei
+  for (int i = threadIdx.x; i < nr; i += 256) {
+    const int64_t r = t0 * K + i;
+    const float* q = dgp + (int64_t)tim[r] * nN;
+    const int e = tei[r];
+    float dg = 0.f;
+    int j = 0;
+    for (; j + 4 <= nN; j += 4) {  // four loads in flight, summed in order
+      const float q0 = q[j], q1 = q[j + 1], q2 = q[j + 2], q3 = q[j + 3];
+      dg += q0;
+      dg += q1;
+      dg += q2;
+      dg += q3;
+    }
+    for (; j < nN; ++j) dg += q[j];
+    s_rows[(i / K) * E + e] = dg;
+  }
+  __syncthreads();
   if (threadIdx.x < nrow) {
     const int64_t t = t0 + threadIdx.x;
-    const int32_t* tm = tim + t * K;
+    const int32_t* te = tei + t * K;
     const float* g = gates + t * K;
+    float* row = s_rows + threadIdx.x * E;
     float sum = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const float* q = dgp + (int64_t)tm[k] * nN;
-      float dg = 0.f;
-      for (int j = 0; j < nN; ++j) dg += q[j];
-      sum += g[k] * dg;
-    }
-    for (int k = 0; k < K; ++k) {
-      const float* q = dgp + (int64_t)tm[k] * nN;
-      float dg = 0.f;
-      for (int j = 0; j < nN; ++j) dg += q[j];
-      s_rows[threadIdx.x * E + tei[t * K + k]] = g[k] * (dg - sum);
-    }
+    for (int k = 0; k < K; ++k) sum += g[k] * row[te[k]];
+    for (int k = 0; k < K; ++k) row[te[k]] = g[k] * (row[te[k]] - sum);
   }
   __syncthreads();
   float* out = dz + t0 * E;
