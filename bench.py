@@ -442,11 +442,7 @@ def main():
         "roofline_dispatch": {"bound": "hbm", "achieved": disp_gbs, "peak": PEAK_HBM_GBS,
                               "unit": "GB/s",
                               "frac": (disp_gbs / PEAK_HBM_GBS) if disp_gbs else None,
-                              "bytes_per_build": dispatch_bytes(cfg), "ms_per_build": disp_ms,
-                              "byte_map_model": {
-                                  "bytes_per_build": dispatch_bytes_byte_map(cfg),
-                                  "frac": (dispatch_bytes_byte_map(cfg) / (disp_ms / 1e3) / 1e9
-                                           / PEAK_HBM_GBS) if disp_ms > 0 else None}},
+                              "bytes_per_build": dispatch_bytes(cfg), "ms_per_build": disp_ms},
         "roofline_by_kernel": {
             k: {"bound": "mfma", "achieved": v["tflops"], "peak": peak, "unit": "TFLOP/s",
                 "frac": v["tflops"] / peak, "traffic": measured_traffic(k, cfg.name),

@@ -31,9 +31,11 @@
  *     moe_last_error() then describes the problem (thread-local text).
  *   - HIP launch errors are returned as MOE_ERR_HIP.
  *   - Limits: 1 <= L; 1 <= E <= 256; 1 <= K <= min(E, 255); L*K < 2^31.
- *     FFN calls also need d % 8 == 0 and h % 8 == 0, and every x, W, A, B,
- *     y, dy, dx, dW pointer 16-byte aligned.  Integer and float32 index/gate
- *     arrays must be 4-byte aligned.
+ *     FFN calls also need d % 8 == 0 and h % 8 == 0, d and h at most
+ *     MOE_MAX_WIDTH (in-tile byte offsets of the GEMM epilogues are 32-bit),
+ *     and every x, W, A, B, y, dy, dx, dW pointer 16-byte aligned.  Integer
+ *     and float32 index/gate arrays must be 4-byte aligned.  Shapes outside
+ *     these limits return MOE_ERR_UNSUPPORTED.
  *   - Router logits must be finite; NaN or infinite logits give unspecified
  *     (but memory-safe) results.
  *   - Results are deterministic: repeated calls on the same inputs produce
@@ -56,6 +58,9 @@ enum {
   MOE_ERR_WORKSPACE = 3,   /* *ws_bytes smaller than the queried size       */
   MOE_ERR_HIP = 4          /* a HIP runtime call or launch failed           */
 };
+
+/* Largest model width d and expert hidden width h the FFN calls accept. */
+#define MOE_MAX_WIDTH 1048576
 
 /* Element type of x, W1, W3, W2, A, B, y, dy, dx, dW1, dW3, dW2.
  * Router logits and gates are always float32; accumulation is float32. */

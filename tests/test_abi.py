@@ -110,6 +110,11 @@ def test_routing_shape_errors(lib, kw, code):
     (dict(h=-8), B.MOE_ERR_INVALID_ARG),
     (dict(d=60), B.MOE_ERR_UNSUPPORTED),
     (dict(h=100), B.MOE_ERR_UNSUPPORTED),
+    # in-tile byte offsets of the GEMM epilogues are 32-bit: widths are capped
+    (dict(d=(1 << 20) + 8), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=(1 << 20) + 8), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=1 << 24), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=(1 << 20) + 8, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_ffn_shape_errors(lib, kw, code):
     assert call_fwd(lib, shp(**kw))[0] == code
@@ -196,3 +201,25 @@ def test_profile_calls_without_gpu(lib):
     n = ctypes.c_int(-1)
     assert lib.moe_profile_read(None, 0, ctypes.byref(n)) == B.MOE_OK
     assert n.value >= 0
+
+
+def test_largest_widths_accepted(lib):
+    """d = h = MOE_MAX_WIDTH passes validation (the workspace query answers)."""
+    for dt in (B.MOE_BF16, B.MOE_F32):
+        rc, need = call_fwd(lib, shp(L=256, d=1 << 20, h=1 << 20, dtype=dt), ws=None)
+        assert rc == B.MOE_OK and need > 0
+
+
+def test_binding_rejects_host_or_mistyped_tensors(lib):
+    """The Python binding checks device placement, dtype, size and contiguity
+    before it reaches the C ABI."""
+    import torch
+    s = shp(L=16, d=64, h=128, E=4, K=2)
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
+    with pytest.raises(B.MoEError, match="device tensor"):
+        B.moe_dispatch_build(s, torch.zeros(16, 4), i32(32), i32(5), i32(32), i32(32),
+                             torch.zeros(32))
+    meta = dict(dtype=torch.float32, device="meta")
+    with pytest.raises(B.MoEError):
+        B.moe_dispatch_build(s, torch.empty(16, 4, **meta), i32(32), i32(5), i32(32), i32(32),
+                             torch.zeros(32))

@@ -103,6 +103,52 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _dt(shape):
+    return torch.float32 if shape.dtype == MOE_F32 else torch.bfloat16
+
+
+def _want(name, t, dtype, numel, optional=False):
+    """A tensor argument must be a contiguous device tensor of the expected
+    element type and size (raw integer addresses pass unchecked)."""
+    if t is None:
+        if optional:
+            return
+        raise MoEError(MOE_ERR_INVALID_ARG, f"{name} is None")
+    if isinstance(t, int):
+        return
+    if not t.is_cuda:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"{name} must be {dtype} (got {t.dtype})")
+    if t.numel() != numel:
+        raise MoEError(MOE_ERR_INVALID_ARG, f"{name} must hold {numel} elements (got {t.numel()})")
+    if not t.is_contiguous():
+        raise MoEError(MOE_ERR_INVALID_ARG, f"{name} must be contiguous")
+
+
+def _check_routing_args(shape, eti, offsets, tei, tim, gates):
+    L, E, K = shape.L, shape.E, shape.K
+    _want("expert_token_indices", eti, torch.int32, L * K)
+    _want("expert_token_offsets", offsets, torch.int32, E + 1)
+    _want("token_expert_indices", tei, torch.int32, L * K)
+    _want("token_index_map", tim, torch.int32, L * K)
+    _want("gates", gates, torch.float32, L * K)
+
+
+def _check_ffn_args(shape, x, W1, W3, W2, **outs):
+    L, d, h, E, K = shape.L, shape.d, shape.h, shape.E, shape.K
+    dt = _dt(shape)
+    glu = shape.act == MOE_SWIGLU
+    _want("x", x, dt, L * d)
+    _want("W1", W1, dt, E * d * h)
+    _want("W3", W3, dt, E * d * h, optional=not glu)
+    _want("W2", W2, dt, E * h * d)
+    sizes = {"y": L * d, "dy": L * d, "dx": L * d, "A": L * K * h, "B": L * K * h,
+             "dW1": E * d * h, "dW3": E * d * h, "dW2": E * h * d}
+    for name, t in outs.items():
+        _want(name, t, dt, sizes[name], optional=(not glu and name in ("B", "dW3")))
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -141,6 +187,8 @@ def workspace_bytes(name: str, shape: Shape) -> int:
 
 def moe_dispatch_build(shape, logits, eti, offsets, tei, tim, gates, ws=None, stream=None):
     lib = load_library()
+    _want("logits", logits, torch.float32, shape.L * shape.E)
+    _check_routing_args(shape, eti, offsets, tei, tim, gates)
     args = [_ptr(logits), _ptr(eti), _ptr(offsets), _ptr(tei), _ptr(tim), _ptr(gates)]
     return _run(lib.moe_dispatch_build, shape, args, ws, stream, logits.device)
 
@@ -148,6 +196,8 @@ def moe_dispatch_build(shape, logits, eti, offsets, tei, tim, gates, ws=None, st
 def moe_ffn_forward(shape, x, W1, W3, W2, eti, offsets, tei, tim, gates, y, A, B,
                     ws=None, stream=None):
     lib = load_library()
+    _check_routing_args(shape, eti, offsets, tei, tim, gates)
+    _check_ffn_args(shape, x, W1, W3, W2, y=y, A=A, B=B)
     args = [_ptr(x), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(eti), _ptr(offsets), _ptr(tei),
             _ptr(tim), _ptr(gates), _ptr(y), _ptr(A), _ptr(B)]
     return _run(lib.moe_ffn_forward, shape, args, ws, stream, x.device)
@@ -157,6 +207,9 @@ def moe_ffn_backward(shape, dy, x, W1, W3, W2, eti, offsets, tei, tim, gates, A,
                      dx, dW1, dW3, dW2, dlogits=None, ws=None, stream=None):
     """dlogits: optional [L, E] float32 output, the router-logit gradient."""
     lib = load_library()
+    _check_routing_args(shape, eti, offsets, tei, tim, gates)
+    _check_ffn_args(shape, x, W1, W3, W2, dy=dy, A=A, B=B, dx=dx, dW1=dW1, dW3=dW3, dW2=dW2)
+    _want("dlogits", dlogits, torch.float32, shape.L * shape.E, optional=True)
     args = [_ptr(dy), _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(eti), _ptr(offsets),
             _ptr(tei), _ptr(tim), _ptr(gates), _ptr(A), _ptr(B), _ptr(dx), _ptr(dW1),
             _ptr(dW3), _ptr(dW2), _ptr(dlogits)]

@@ -57,6 +57,19 @@ int check_ffn_shape(const moe_shape* s) {
   if (s->d < 1 || s->h < 1) return fail(MOE_ERR_INVALID_ARG, "d and h must be >= 1 (d=%d, h=%d)", s->d, s->h);
   if (s->d % 8 != 0 || s->h % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "d and h must be multiples of 8 (d=%d, h=%d)", s->d, s->h);
+  // The GEMM epilogues form in-tile byte offsets (256 rows of d or h
+  // elements) in 32 bits.
+  if (s->d > MOE_MAX_WIDTH || s->h > MOE_MAX_WIDTH)
+    return fail(MOE_ERR_UNSUPPORTED, "d and h must be <= %d (d=%d, h=%d)", MOE_MAX_WIDTH, s->d,
+                s->h);
+  // Every launch grid must fit the 32-bit grid size.
+  const int64_t cd = ((int64_t)s->d + 255) / 256, ch = ((int64_t)s->h + 127) / 128;
+  const int64_t route_tiles = (s->L * s->K + 255) / 256 + s->E;
+  const int64_t pass_tiles = (s->L + 255) / 256 + s->E;
+  const int64_t weight_tiles = (int64_t)s->E * cd * ch;
+  if (route_tiles * ch > INT32_MAX / 2 || pass_tiles * cd > INT32_MAX / 2 ||
+      weight_tiles > INT32_MAX / 2)
+    return fail(MOE_ERR_UNSUPPORTED, "shape needs more workgroups than one launch holds");
   return MOE_OK;
 }
 
