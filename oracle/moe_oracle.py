@@ -303,22 +303,26 @@ def router_backward(dy, x, W1, W3, W2, eti, offsets, tei, tim, gates, act):
 
 # ---------------------------------------------------------------------------
 # Sampled evaluation for shapes too large to run whole on the host.
-# Each function computes the same quantities as ffn_forward / ffn_backward
-# for a subset of outputs; tests check them against the full versions.
+# Each function computes the same quantities as ffn_forward / ffn_backward /
+# router_backward for a subset of outputs, with the same formulas applied to
+# the subset's rows; rows that share an expert are multiplied together.
+# Tests check them against the full versions.
 # ---------------------------------------------------------------------------
 
 def route_rows_forward(p_rows, x, W1, W3, eti, offsets, act):
-    """A[p], B[p] (float64) for the listed route rows p."""
+    """A[p], B[p] (float64) for the listed route rows p: row p belongs to the
+    expert whose interval of offsets holds it and reads x[eti[p]]."""
     p_rows = np.asarray(p_rows, dtype=np.int64)
     e_of = np.searchsorted(np.asarray(offsets, dtype=np.int64), p_rows, side="right") - 1
     h = W1.shape[2]
     A = np.zeros((p_rows.size, h))
     B = np.zeros((p_rows.size, h)) if act == SWIGLU else None
-    for i, (p, e) in enumerate(zip(p_rows, e_of)):
-        xt = np.asarray(x[eti[p]], dtype=np.float64)
-        A[i] = xt @ np.asarray(W1[e], dtype=np.float64)
+    for e in np.unique(e_of):
+        sel = np.flatnonzero(e_of == e)
+        X = _f64(x[np.asarray(eti)[p_rows[sel]]])
+        A[sel] = X @ _f64(W1[e])
         if act == SWIGLU:
-            B[i] = xt @ np.asarray(W3[e], dtype=np.float64)
+            B[sel] = X @ _f64(W3[e])
     return A, B
 
 
@@ -326,37 +330,40 @@ def token_rows(tokens, dy, x, W1, W3, W2, tei, tim, gates, act):
     """y[t] and dx[t] (float64) for the listed tokens.
 
     Every quantity of one route depends only on its own token row, so the
-    rows of y and dx can be computed token by token with the same formulas
-    as ffn_forward / ffn_backward.
+    rows of y and dx follow from the same formulas as ffn_forward /
+    ffn_backward applied to the listed tokens' routes alone.  Slot k of each
+    token is added in ascending k; the tokens whose slot-k expert is e are
+    evaluated together.
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     K = tei.shape[1]
     d = x.shape[1]
+    X = _f64(x[tokens])
+    DY = _f64(dy[tokens]) if dy is not None else None
     y = np.zeros((tokens.size, d))
     dx = np.zeros((tokens.size, d))
-    for i, t in enumerate(tokens):
-        xt = np.asarray(x[t], dtype=np.float64)
-        dyt = np.asarray(dy[t], dtype=np.float64) if dy is not None else None
-        for k in range(K):
-            e = int(tei[t, k])
-            g = float(gates[t, k])
-            w1 = np.asarray(W1[e], dtype=np.float64)
-            w2 = np.asarray(W2[e], dtype=np.float64)
-            a = xt @ w1
-            b = xt @ np.asarray(W3[e], dtype=np.float64) if act == SWIGLU else None
+    for k in range(K):
+        ek = np.asarray(tei)[tokens, k]
+        gk = np.asarray(gates, dtype=np.float64)[tokens, k]
+        for e in np.unique(ek):
+            sel = np.flatnonzero(ek == e)
+            g = gk[sel][:, None]
+            w1, w2 = _f64(W1[e]), _f64(W2[e])
+            w3 = _f64(W3[e]) if act == SWIGLU else None
+            a = X[sel] @ w1
+            b = X[sel] @ w3 if act == SWIGLU else None
             G = _glu(a, b, act)
-            y[i] += g * (G @ w2)
-            if dyt is None:
+            y[sel] += g * (G @ w2)
+            if DY is None:
                 continue
-            dG = (g * dyt) @ w2.T
+            dG = (g * DY[sel]) @ w2.T
             if act == SWIGLU:
-                w3 = np.asarray(W3[e], dtype=np.float64)
                 dA = dG * b * _dsilu(a)
                 dB = dG * _silu(a)
-                dx[i] += dA @ w1.T + dB @ w3.T
+                dx[sel] += dA @ w1.T + dB @ w3.T
             else:
                 dA = dG * _dsilu(a)
-                dx[i] += dA @ w1.T
+                dx[sel] += dA @ w1.T
     return y, dx
 
 
@@ -403,21 +410,25 @@ def dw_columns(e, cols, dy, x, W1, W3, W2, eti, offsets, tim, tei, gates, act):
 
 def router_rows(tokens, dy, x, W1, W3, W2, tei, gates, act, E):
     """Rows of router_backward (float64 [len(tokens), E]) for the listed
-    tokens: a token's logit gradient needs only its own K routes."""
+    tokens: a token's logit gradient needs only its own K routes, evaluated
+    slot by slot, the tokens that share the slot's expert together."""
     tokens = np.asarray(tokens, dtype=np.int64)
     K = tei.shape[1]
+    X = _f64(x[tokens])
+    DY = _f64(dy[tokens])
+    dg = np.zeros((tokens.size, K))
+    for k in range(K):
+        ek = np.asarray(tei)[tokens, k]
+        for e in np.unique(ek):
+            sel = np.flatnonzero(ek == e)
+            a = X[sel] @ _f64(W1[e])
+            b = X[sel] @ _f64(W3[e]) if act == SWIGLU else None
+            O = _glu(a, b, act) @ _f64(W2[e])
+            dg[sel, k] = (DY[sel] * O).sum(axis=1)
+    g = np.asarray(gates, dtype=np.float64)[tokens]
     dz = np.zeros((tokens.size, E))
-    for i, t in enumerate(tokens):
-        xt = np.asarray(x[t], dtype=np.float64)
-        dyt = np.asarray(dy[t], dtype=np.float64)
-        dg = np.zeros((1, K))
-        for k in range(K):
-            e = int(tei[t, k])
-            a = xt @ np.asarray(W1[e], dtype=np.float64)
-            b = xt @ np.asarray(W3[e], dtype=np.float64) if act == SWIGLU else None
-            dg[0, k] = dyt @ (_glu(a, b, act) @ np.asarray(W2[e], dtype=np.float64))
-        g = np.asarray(gates[t], dtype=np.float64)[None, :]
-        dz[i, np.asarray(tei[t], dtype=np.int64)] = _softmax_backward(g, dg)[0]
+    np.put_along_axis(dz, np.asarray(tei, dtype=np.int64)[tokens], _softmax_backward(g, dg),
+                      axis=1)
     return dz
 
 

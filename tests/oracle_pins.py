@@ -320,15 +320,17 @@ def check_sampled_consistency(orc):
     for i, (L, d, h, E, K, act, ints) in enumerate(DENSE_CASES):
         logits, x, W1, W3, W2, dy = tiny_inputs(L, d, h, E, K, act, 60 + i, ints)
         o = _run_oracle(orc, logits, x, W1, W3, W2, dy, K, act)
-        toks = np.array([0, L // 2, L - 1])
-        y, dx = orc.token_rows(toks, dy, x, W1, W3, W2, o["tei"], o["tim"], o["gates"], act)
-        assert relerr(y, o["y"][toks]) < 1e-12, i
-        assert relerr(dx, o["dx"][toks]) < 1e-12, i
-        prow = np.array([0, L * K // 3, L * K - 1])
-        A, B = orc.route_rows_forward(prow, x, W1, W3, o["eti"], o["off"], act)
-        assert relerr(A, o["A"][prow]) < 1e-12, i
-        if act == SWIGLU:
-            assert relerr(B, o["B"][prow]) < 1e-12, i
+        # a sample in which several tokens share a slot's expert, and every token
+        toks = np.array([L - 1, 0, L // 2, 1, 2, 3, L // 3, 5, 7])
+        for tt in (toks, np.arange(L)):
+            y, dx = orc.token_rows(tt, dy, x, W1, W3, W2, o["tei"], o["tim"], o["gates"], act)
+            assert relerr(y, o["y"][tt]) < 1e-12, i
+            assert relerr(dx, o["dx"][tt]) < 1e-12, i
+        for prow in (np.array([L * K - 1, 0, L * K // 3, 1, 2, L * K // 2]), np.arange(L * K)):
+            A, B = orc.route_rows_forward(prow, x, W1, W3, o["eti"], o["off"], act)
+            assert relerr(A, o["A"][prow]) < 1e-12, i
+            if act == SWIGLU:
+                assert relerr(B, o["B"][prow]) < 1e-12, i
         for e in range(E):
             cols = np.array([0, h - 1])
             c1, c3, r2 = orc.dw_columns(e, cols, dy, x, W1, W3, W2, o["eti"], o["off"],
@@ -388,9 +390,14 @@ def check_router_special_cases(orc):
     g64 = _gates64(logits, o["tei"])
     dz = orc.router_backward(dy, x, W1, W3, W2, o["eti"], o["off"], o["tei"], o["tim"], g64, SILU)
     assert np.abs(dz.sum(axis=1)).max() <= 1e-12 * max(1.0, np.abs(dz).max())
-    # sampled rows agree with the full gradient
-    toks = np.array([0, 12, 24])
-    rows = orc.router_rows(toks, dy, x, W1, W3, W2, o["tei"], o["gates"], SILU, 6)
+    # sampled rows agree with the full gradient (a few tokens; every token)
+    for toks in (np.array([24, 0, 12, 1, 2, 3, 4]), np.arange(25)):
+        rows = orc.router_rows(toks, dy, x, W1, W3, W2, o["tei"], o["gates"], SILU, 6)
+        assert relerr(rows, o["dlogits"][toks]) < 1e-12
+    logits, x, W1, W3, W2, dy = tiny_inputs(19, 5, 6, 4, 2, SWIGLU, 33)
+    o = _run_oracle(orc, logits, x, W1, W3, W2, dy, 2, SWIGLU)
+    toks = np.array([18, 3, 0, 7, 8, 9])
+    rows = orc.router_rows(toks, dy, x, W1, W3, W2, o["tei"], o["gates"], SWIGLU, 4)
     assert relerr(rows, o["dlogits"][toks]) < 1e-12
 
 

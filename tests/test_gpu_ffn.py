@@ -77,14 +77,18 @@ def test_skewed_small_f32():
     run_full_parity(cfg, 5, require_gpu())
 
 
-@pytest.mark.parametrize("ci", [2, 3])
-def test_configs_sampled(ci):
-    run_sampled_parity(W.CONFIGS[ci], ci, require_gpu())
+def test_config2_full():
+    """The 16K-token SiLU layer (E = 8, K = 2, bf16), whole tensors."""
+    say("  config 2, whole tensors")
+    run_full_parity(W.CONFIGS[2], 2, require_gpu())
 
 
-@pytest.mark.parametrize("ci", [4, 5])
+@pytest.mark.parametrize("ci", [3, 4, 5])
 def test_large_configs_sampled(ci):
-    run_sampled_parity(W.CONFIGS[ci], ci, require_gpu(), n_tokens=24, n_experts=1, n_cols=3)
+    """4,096 seeded tokens' y, dx, dlogits and A/B rows; whole dW of the
+    heaviest, lightest and one random expert (a tile-covering column subset
+    where the oracle would take minutes); exact zeros for empty experts."""
+    run_sampled_parity(W.CONFIGS[ci], ci, require_gpu())
 
 
 def test_bitwise_repeatable_and_poisoned_workspace():

@@ -54,8 +54,17 @@ MUTATIONS = [
      "return _silu(Ae) if act == SILU else _silu(Ae) * Be",
      "return _silu(Ae) if act == SILU else _silu(Be) * Ae"),
     ("sampled y without gate",
-     "y[i] += g * (G @ w2)",
-     "y[i] += (G @ w2)"),
+     "y[sel] += g * (G @ w2)",
+     "y[sel] += (G @ w2)"),
+    ("sampled A rows of the first selected expert only",
+     "for e in np.unique(e_of):\n        sel = np.flatnonzero(e_of == e)",
+     "for e in np.unique(e_of)[:1]:\n        sel = np.flatnonzero(e_of >= e)"),
+    ("sampled dx with the slot's gate of slot 0",
+     "gk = np.asarray(gates, dtype=np.float64)[tokens, k]",
+     "gk = np.asarray(gates, dtype=np.float64)[tokens, 0]"),
+    ("sampled router rows: tokens of one expert take the first token's output",
+     "            dg[sel, k] = (DY[sel] * O).sum(axis=1)",
+     "            dg[sel, k] = (DY[sel] * O[:1]).sum(axis=1)"),
     ("sampled dW2 rows without gate",
      "dO = g[:, None] * np.asarray(dy[toks], dtype=np.float64)",
      "dO = np.asarray(dy[toks], dtype=np.float64)"),
