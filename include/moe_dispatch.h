@@ -110,6 +110,27 @@ int moe_dispatch_build(const moe_shape* s, const float* logits,
                        float* gates, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * moe_dispatch_build_noalloc -- moe_dispatch_build without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same inputs, outputs, validation and results as moe_dispatch_build.  The
+ * workspace is a device array owned by the library, MOE_NOALLOC_WS_BYTES
+ * bytes per GPU, held from the first call on that GPU until the process
+ * ends; the call itself allocates nothing.  A shape whose moe_dispatch_build
+ * workspace exceeds MOE_NOALLOC_WS_BYTES returns MOE_ERR_UNSUPPORTED (the
+ * layer with L = 1,048,576 tokens, E = 64, K = 6 needs 21 MiB and fits).
+ * Every call on one GPU uses the same array: calls that can overlap in time
+ * on one GPU (unordered streams, several host threads) race and give
+ * undefined results; calls ordered on one stream are safe.
+ */
+#define MOE_NOALLOC_WS_BYTES (24u << 20)
+int moe_dispatch_build_noalloc(const moe_shape* s, const float* logits,
+                               int32_t* expert_token_indices, int32_t* expert_token_offsets,
+                               int32_t* token_expert_indices, int32_t* token_index_map,
+                               float* gates, void* stream);
+
+/*
  * moe_ffn_forward -- expert FFN forward with on-the-fly gather and
  * gate-weighted aggregation.
  *

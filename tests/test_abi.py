@@ -223,3 +223,28 @@ def test_binding_rejects_host_or_mistyped_tensors(lib):
     with pytest.raises(B.MoEError):
         B.moe_dispatch_build(s, torch.empty(16, 4, **meta), i32(32), i32(5), i32(32), i32(32),
                              torch.zeros(32))
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch_array(lib):
+    """moe_dispatch_build_noalloc validates like moe_dispatch_build and refuses
+    a shape whose workspace exceeds the library's scratch array, before any
+    HIP call."""
+    big = B.make_shape(1 << 22, 8, 8, 64, 6)        # needs about 84 MiB
+    n = ctypes.c_size_t(0)
+    assert lib.moe_dispatch_build(ctypes.byref(big), *([FAKE] * 6), None, ctypes.byref(n),
+                                  None) == B.MOE_OK
+    assert n.value > B.MOE_NOALLOC_WS_BYTES
+    assert lib.moe_dispatch_build_noalloc(ctypes.byref(big), *([FAKE] * 6), None) \
+        == B.MOE_ERR_UNSUPPORTED
+    assert "scratch" in lib.moe_last_error().decode()
+    # the 1M-token, 64-expert routing fits
+    n = ctypes.c_size_t(0)
+    fit = B.make_shape(1 << 20, 8, 8, 64, 6)
+    assert lib.moe_dispatch_build(ctypes.byref(fit), *([FAKE] * 6), None, ctypes.byref(n),
+                                  None) == B.MOE_OK
+    assert n.value <= B.MOE_NOALLOC_WS_BYTES
+    for kw, code in ((dict(L=0), B.MOE_ERR_INVALID_ARG), (dict(E=257, K=2), B.MOE_ERR_UNSUPPORTED)):
+        assert lib.moe_dispatch_build_noalloc(ctypes.byref(shp(**kw)), *([FAKE] * 6), None) == code
+    p = [FAKE] * 6
+    p[3] = FAKE + 2
+    assert lib.moe_dispatch_build_noalloc(ctypes.byref(shp()), *p, None) == B.MOE_ERR_INVALID_ARG

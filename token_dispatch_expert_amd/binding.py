@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libm
 
 EXPORTED = (
     "moe_dispatch_build",
+    "moe_dispatch_build_noalloc",
     "moe_ffn_forward",
     "moe_ffn_backward",
     "moe_last_error",
@@ -70,10 +71,12 @@ def load_library(path: str = LIB_PATH):
     SZ = ctypes.POINTER(ctypes.c_size_t)
     S = ctypes.POINTER(Shape)
     lib.moe_dispatch_build.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_dispatch_build_noalloc.argtypes = [S, P, P, P, P, P, P, P]
     lib.moe_ffn_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_ffn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ,
                                      P]
-    for f in ("moe_dispatch_build", "moe_ffn_forward", "moe_ffn_backward",
+    for f in ("moe_dispatch_build", "moe_dispatch_build_noalloc", "moe_ffn_forward",
+              "moe_ffn_backward",
               "moe_profile_enable", "moe_profile_reset", "moe_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
     lib.moe_last_error.restype = ctypes.c_char_p
@@ -191,6 +194,21 @@ def moe_dispatch_build(shape, logits, eti, offsets, tei, tim, gates, ws=None, st
     _check_routing_args(shape, eti, offsets, tei, tim, gates)
     args = [_ptr(logits), _ptr(eti), _ptr(offsets), _ptr(tei), _ptr(tim), _ptr(gates)]
     return _run(lib.moe_dispatch_build, shape, args, ws, stream, logits.device)
+
+
+def moe_dispatch_build_noalloc(shape, logits, eti, offsets, tei, tim, gates, stream=None):
+    """moe_dispatch_build with the library's own scratch array as workspace:
+    nothing is allocated (see include/moe_dispatch.h for the size limit and
+    the rule that calls overlapping on one GPU race)."""
+    lib = load_library()
+    _want("logits", logits, torch.float32, shape.L * shape.E)
+    _check_routing_args(shape, eti, offsets, tei, tim, gates)
+    _check(lib.moe_dispatch_build_noalloc(ctypes.byref(shape), _ptr(logits), _ptr(eti),
+                                          _ptr(offsets), _ptr(tei), _ptr(tim), _ptr(gates),
+                                          _stream(stream)))
+
+
+MOE_NOALLOC_WS_BYTES = 24 << 20
 
 
 def moe_ffn_forward(shape, x, W1, W3, W2, eti, offsets, tei, tim, gates, y, A, B,

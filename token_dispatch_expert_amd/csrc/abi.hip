@@ -146,6 +146,37 @@ Profiler& prof() {
   return p;
 }
 
+// ------------------------------------------------ allocation-free dispatch
+// Workspace of moe_dispatch_build_noalloc.  Every GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -196,6 +227,34 @@ int moe_dispatch_build(const moe_shape* s, const float* logits, int32_t* eti, in
   hipError_t e = moe::launch_dispatch(pl, s->L, s->E, s->K, logits, eti, offsets, tei, tim, gates,
                                       static_cast<char*>(ws), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "moe_dispatch_build launch");
+  return MOE_OK;
+}
+
+int moe_dispatch_build_noalloc(const moe_shape* s, const float* logits, int32_t* eti,
+                               int32_t* offsets, int32_t* tei, int32_t* tim, float* gates,
+                               void* stream) {
+  g_err.clear();
+  int rc = check_routing(s);
+  if (rc != MOE_OK) return rc;
+  const PtrCheck pc[] = {{"logits", logits, 4}, {"expert_token_indices", eti, 4},
+                         {"expert_token_offsets", offsets, 4}, {"token_expert_indices", tei, 4},
+                         {"token_index_map", tim, 4}, {"gates", gates, 4}};
+  rc = check_ptrs(pc, 6);
+  if (rc != MOE_OK) return rc;
+  const moe::DispatchPlan pl = moe::plan_dispatch(s->L, s->E, s->K);
+  if (pl.bytes > (size_t)MOE_NOALLOC_WS_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_dispatch_build_noalloc: this shape needs %zu bytes of workspace, more than "
+                "the %zu bytes of the library's scratch array (use moe_dispatch_build)",
+                pl.bytes, (size_t)MOE_NOALLOC_WS_BYTES);
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != MOE_OK) return rc;
+  // The dispatch kernels write every workspace entry they read, so the
+  // previous call's contents need no clearing.
+  hipError_t e = moe::launch_dispatch(pl, s->L, s->E, s->K, logits, eti, offsets, tei, tim, gates,
+                                      ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_dispatch_build_noalloc launch");
   return MOE_OK;
 }
 
