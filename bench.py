@@ -56,6 +56,17 @@ def kernel_flops(cfg):
     }
 
 
+def mask_words(E):
+    """64-bit expert-mask words per token of the bit-form map: 1 for E <= 64,
+    else the smallest power of two P >= 2 with 64 P >= E."""
+    if E <= 64:
+        return 1
+    P = 2
+    while 64 * P < E:
+        P *= 2
+    return P
+
+
 def dispatch_bytes(cfg):
     """Algorithmic HBM bytes of one dispatch build, for the map representation
     the library uses at this shape.
@@ -63,17 +74,18 @@ def dispatch_bytes(cfg):
     Always: logits read once (4LE), the four L*K int32/float32 outputs
     token_expert_indices, gates, expert_token_indices, token_index_map written
     once (16LK), and the offsets (4(E+1)).
-    E <= 64 and K <= 8 (bit-mask map): each token's 64-bit expert mask and each
-    64-token part's per-expert column (E/8 bytes per token) written once and
-    read once; per-part counts (int32 per expert and part) written and read,
-    256-token tile bases written and read.
-    Otherwise (byte map): E bytes per token written once and read once."""
+    E <= 1024 and K <= 8 (bit-form map): each token's expert mask (W words of
+    8 bytes) and each 64-token part's per-expert column (E/8 bytes per token)
+    written once and read once; per-part counts (int32 per expert and part)
+    written and read, 256-token tile bases written and read.
+    Otherwise (byte map, K > 8): E bytes per token written once and read once."""
     L, E, K = cfg.L, cfg.E, cfg.K
     b = 4 * L * E + 16 * L * K + 4 * (E + 1)
-    if E <= 64 and K <= 8:
+    if E <= 1024 and K <= 8:
         tiles = -(-L // 256)
         parts = 4 * tiles
-        b += 2 * 8 * L + 2 * 8 * E * parts + 2 * 4 * E * parts + 2 * 4 * E * tiles
+        b += (2 * 8 * mask_words(E) * L + 2 * 8 * E * parts + 2 * 4 * E * parts
+              + 2 * 4 * E * tiles)
     else:
         b += 2 * L * E
     return b
@@ -104,7 +116,7 @@ ROCPROF_NAMES = {   # library timer name -> kernel symbol base name in rocprofv3
     "ffn_b0_dw2": "b0_dw2",
     "ffn_b2_dw13": "b2_dw13",
     "ffn_b3_dx": "b3_dx",
-    "dispatch_route_map": "k1_route_mask",     # E <= 64, K <= 8 (the byte-map path is k1_route_map*)
+    "dispatch_route_map": "k1_route_mask",     # E <= 64, K <= 8 (k1_route_wide_mask beyond, k1_route_map* for K > 8)
     "dispatch_scatter": "k3_scatter_mask",
 }
 
@@ -235,7 +247,7 @@ def study_memory(cfg, seed, dev):
 
 def study_dispatch_e(cfg, seed, dev, reps=20):
     """Dispatch build time and HBM rate over E at the workload's L and K."""
-    for E in (8, 16, 32, 64, 128, 256):
+    for E in (8, 16, 32, 64, 128, 256, 512, 1024):
         if E < cfg.K:
             continue
         c = W.MoEConfig(f"{cfg.name}-E{E}", cfg.L, cfg.d, cfg.h, E, cfg.K, cfg.act, cfg.dtype)
@@ -254,7 +266,7 @@ def study_dispatch_e(cfg, seed, dev, reps=20):
         nb = dispatch_bytes(c)
         _emit({"study": "dispatch-e", "L": c.L, "E": E, "K": c.K, "ms_per_build": ms,
                "bytes_per_build": nb, "GB/s": nb / (ms / 1e3) / 1e9,
-               "map": "bit-mask" if (E <= 64 and c.K <= 8) else "byte",
+               "map": f"bit-form, {mask_words(E)} mask word(s) per token" if c.K <= 8 else "byte",
                "kernels_ms": {k: v[1] / reps for k, v in st.items()}})
         del buf, logits
         torch.cuda.empty_cache()

@@ -30,7 +30,8 @@
  *     returns anything but MOE_OK has launched nothing and written nothing.
  *     moe_last_error() then describes the problem (thread-local text).
  *   - HIP launch errors are returned as MOE_ERR_HIP.
- *   - Limits: 1 <= L; 1 <= E <= 256; 1 <= K <= min(E, 255); L*K < 2^31.
+ *   - Limits: 1 <= L; 1 <= E <= 1024; 1 <= K <= min(E, 255), and K <= 8 when
+ *     E > 256; L*K < 2^31.
  *     FFN calls also need d % 8 == 0 and h % 8 == 0, d and h at most
  *     MOE_MAX_WIDTH (in-tile byte offsets of the GEMM epilogues are 32-bit),
  *     and every x, W, A, B, y, dy, dx, dW pointer 16-byte aligned.  Integer

@@ -89,7 +89,8 @@ def shp(**kw):
     (dict(E=0), B.MOE_ERR_INVALID_ARG),
     (dict(K=0), B.MOE_ERR_INVALID_ARG),
     (dict(K=9), B.MOE_ERR_INVALID_ARG),
-    (dict(E=257, K=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=1025, K=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=257, K=9), B.MOE_ERR_UNSUPPORTED),      # K > 8 only up to 256 experts
     (dict(E=256, K=256), B.MOE_ERR_UNSUPPORTED),
     (dict(L=1 << 30, K=2), B.MOE_ERR_UNSUPPORTED),
 ])
@@ -243,8 +244,28 @@ def test_noalloc_rejects_shapes_beyond_the_scratch_array(lib):
     assert lib.moe_dispatch_build(ctypes.byref(fit), *([FAKE] * 6), None, ctypes.byref(n),
                                   None) == B.MOE_OK
     assert n.value <= B.MOE_NOALLOC_WS_BYTES
-    for kw, code in ((dict(L=0), B.MOE_ERR_INVALID_ARG), (dict(E=257, K=2), B.MOE_ERR_UNSUPPORTED)):
+    for kw, code in ((dict(L=0), B.MOE_ERR_INVALID_ARG), (dict(E=1025, K=2), B.MOE_ERR_UNSUPPORTED)):
         assert lib.moe_dispatch_build_noalloc(ctypes.byref(shp(**kw)), *([FAKE] * 6), None) == code
     p = [FAKE] * 6
     p[3] = FAKE + 2
     assert lib.moe_dispatch_build_noalloc(ctypes.byref(shp()), *p, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_library_sources_allocate_nothing():
+    """The library's sources call no allocating HIP routine (the caller owns
+    every buffer; the allocation-free entry point's array is static)."""
+    csrc = os.path.join(ROOT, "token_dispatch_expert_amd", "csrc")
+    banned = re.compile(r"\bhip(Malloc\w*|Free\w*|HostMalloc|ExtMallocWithFlags|MallocAsync|"
+                        r"MemPool\w*)\s*\(")
+    for f in sorted(os.listdir(csrc)):
+        src = open(os.path.join(csrc, f)).read()
+        src = re.sub(r"//.*", "", src)
+        assert not banned.search(src), f"{f} calls an allocating HIP routine"
+
+
+def test_expert_counts_up_to_1024_accepted(lib):
+    for E, K in ((257, 8), (512, 6), (1024, 8), (1024, 1), (256, 255)):
+        rc, need = call_build(lib, shp(E=E, K=K), ws=None)
+        assert rc == B.MOE_OK and need > 0, (E, K)
+        assert call_fwd(lib, shp(E=E, K=K), ws=None)[0] == B.MOE_OK
+        assert call_bwd(lib, shp(E=E, K=K), ws=None)[0] == B.MOE_OK

@@ -7,8 +7,9 @@ its roofline figures), against closed forms for the layer:
 * one dispatch build in the method's byte-map layout moves 4LE (logits) +
   3LE (map written once, read twice) + 16LK (the four L*K outputs) + 4(E+1)
   bytes: 544 bytes per token at L = 1M, E = 64, K = 6;
-* the bit-mask layout replaces the 3LE map bytes by 16L (token masks) and
-  the per-part columns, counts and tile bases.
+* the bit-form layout replaces the 3LE map bytes by 16 W L (token masks of W
+  64-bit words, written and read) and the per-part columns, counts and tile
+  bases.
 """
 
 import bench
@@ -55,6 +56,14 @@ def test_dispatch_bytes_bit_mask():
               + 2 * 8 * E * parts                      # per-part columns
               + 2 * 4 * E * parts + 2 * 4 * E * tiles)  # part counts, tile bases
     assert bench.dispatch_bytes(cfg) == expect == 413_139_204
-    # byte-map configurations (E > 64) count the map as 2LE (written, read)
-    big = W.small_config(4096, 64, 64, 128, 6, W.SWIGLU, W.BF16)
-    assert bench.dispatch_bytes(big) == 4 * 4096 * 128 + 16 * 4096 * 6 + 4 * 129 + 2 * 4096 * 128
+    # wide bit form: W mask words per token (W = 2, 4, 8, 16 for E up to 128,
+    # 256, 512, 1024), then the same per-part columns, counts and tile bases
+    for E, Wd in ((128, 2), (200, 4), (256, 4), (512, 8), (1000, 16), (1024, 16)):
+        c = W.small_config(4096, 64, 64, E, 6, W.SWIGLU, W.BF16)
+        assert bench.mask_words(E) == Wd
+        assert bench.dispatch_bytes(c) == (4 * 4096 * E + 16 * 4096 * 6 + 4 * (E + 1)
+                                           + 2 * 8 * Wd * 4096 + 2 * 8 * E * 64
+                                           + 2 * 4 * E * 64 + 2 * 4 * E * 16)
+    # byte-map configurations (K > 8) count the map as 2LE (written, read)
+    big = W.small_config(4096, 64, 64, 128, 12, W.SWIGLU, W.BF16)
+    assert bench.dispatch_bytes(big) == 4 * 4096 * 128 + 16 * 4096 * 12 + 4 * 129 + 2 * 4096 * 128

@@ -66,8 +66,9 @@ def test_bf16_gemm_kernels_do_not_spill(asm):
 
 def test_no_copy_wait_before_fragment_reads(asm):
     """Once a k-tile's copies (global_load_lds) are out, no LDS read or MFMA
-    may follow a vmcnt wait before the barrier that ends the k-tile: the
-    copies only have to land by that barrier."""
+    may follow a vmcnt wait in the same basic block before the barrier that
+    ends the k-tile: the copies only have to land by that barrier (the loop's
+    own waits sit at the end of a block that branches to the barrier)."""
     checked = 0
     for name, body in _bf16_gemms(_kernels(asm)).items():
         inflight = waited = False
@@ -76,6 +77,8 @@ def test_no_copy_wait_before_fragment_reads(asm):
                 inflight, waited = True, False
             elif line.startswith("s_barrier"):
                 inflight = waited = False
+            elif line.startswith((".LBB", "s_branch", "s_cbranch")):
+                waited = False          # a new basic block
             elif inflight and line.startswith("s_waitcnt") and "vmcnt" in line:
                 waited = True
             elif inflight and line.startswith(("ds_read", "v_mfma")):

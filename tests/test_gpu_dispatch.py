@@ -65,6 +65,17 @@ EDGE = [
     (1100, 256, 1, "ties"),         # largest E, K = 1, ties
     (900, 96, 8, "signed_zero"),    # lane-pair router, signed zeros
     (3000, 252, 6, "misaligned"),   # lane-quad router, logits not 16-byte aligned
+    (2000, 512, 6, "normal"),       # eight mask words per token
+    (1500, 1024, 8, "normal"),      # largest E: sixteen mask words, four routing rounds
+    (700, 1000, 3, "normal"),       # E not a multiple of 64: last word partly empty
+    (999, 777, 8, "ties"),          # ties at the K-th value across sixteen lanes
+    (600, 1024, 1, "ties"),         # largest E, K = 1
+    (3000, 500, 4, "misaligned"),   # logits not 16-byte aligned, E = 500
+    (1000, 300, 2, "signed_zero"),  # signed zeros, eight words
+    (5000, 1024, 8, "empty_mid"),   # expert 7 never chosen, 1024 experts
+    (4096, 640, 5, "all_one"),      # every token on expert 3
+    (1, 1024, 8, "normal"),         # one token
+    (129, 65, 8, "normal"),         # smallest wide E, ragged tile
 ]
 
 

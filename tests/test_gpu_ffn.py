@@ -36,6 +36,9 @@ SMALL = [
     (300, 64, 128, 32, 12, SWIGLU, W.BF16),   # K = 12 > 8: byte-map router, twelve slot passes
     (100, 64, 64, 256, 1, SWIGLU, W.BF16),    # K = 1, E = 256: most experts empty (dW exactly 0)
     (64, 8, 8, 4, 2, SWIGLU, W.BF16),         # d = h = 8: one 16-byte chunk per row
+    (800, 64, 128, 512, 6, SWIGLU, W.BF16),   # E = 512: about 9 routes per expert
+    (600, 64, 64, 1024, 8, SILU, W.F32),      # E = 1024: many empty experts, fp32
+    (300, 72, 136, 1000, 4, SWIGLU, W.BF16),  # E = 1000, ragged widths
 ]
 
 

@@ -40,8 +40,10 @@ int check_routing(const moe_shape* s) {
   if (s->E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", s->E);
   if (s->K < 1) return fail(MOE_ERR_INVALID_ARG, "K must be >= 1 (got %d)", s->K);
   if (s->K > s->E) return fail(MOE_ERR_INVALID_ARG, "K (%d) must not exceed E (%d)", s->K, s->E);
-  if (s->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 256 (got %d)", s->E);
+  if (s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024 (got %d)", s->E);
   if (s->K > 255) return fail(MOE_ERR_UNSUPPORTED, "K must be <= 255 (got %d)", s->K);
+  if (s->E > 256 && s->K > 8)
+    return fail(MOE_ERR_UNSUPPORTED, "K must be <= 8 when E > 256 (got E=%d, K=%d)", s->E, s->K);
   if (s->L > (int64_t)INT32_MAX / s->K)
     return fail(MOE_ERR_UNSUPPORTED, "L*K must be < 2^31 (L=%lld, K=%d)", (long long)s->L, s->K);
   return MOE_OK;

@@ -165,166 +165,6 @@ __global__ __launch_bounds__(256) void k1_route_map(const float* __restrict__ lo
   }
 }
 
-// Step 1 for 64 < E <= 256 and K <= 8 (byte map): P lanes per token (P = 2
-// for E <= 128, 4 otherwise), lane q of a token holding the logits of
-// experts 64q .. 64q+63 in registers.  Each lane keeps its slice's KM
-// largest values with the med3 network; the P lists are merged across the
-// token's lanes (the partner's list is inserted into one's own, butterfly
-// order), giving the token's K-th value thr.  Each lane then marks its
-// experts with logit >= thr; surplus marks can only be ties with thr and are
-// dropped from the highest expert ids (highest lane first), and a shortfall
-// (NaN logits, outside the contract) is filled with the lowest unmarked ids,
-// so every token gets exactly K valid experts.  Slots follow the lanes'
-// order, hence ascending expert id.
-template <int P, int KM, bool VEC>
-__global__ __launch_bounds__(256) void k1_route_wide(const float* __restrict__ logits, int64_t L,
-                                                     int E, int K, int T, int C, int64_t Lpad,
-                                                     int32_t* __restrict__ tei,
-                                                     float* __restrict__ gates,
-                                                     uint8_t* __restrict__ map,
-                                                     int32_t* __restrict__ tilecnt) {
-  extern __shared__ uint4 smap_v[];
-  uint8_t* smap = reinterpret_cast<uint8_t*>(smap_v);
-  const int tile = blockIdx.x;
-  const int64_t t0 = (int64_t)tile * T;
-  const int nvec = (E * T) >> 4;
-  for (int i = threadIdx.x; i < nvec; i += 256) smap_v[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-
-  const int q = threadIdx.x % P;
-  const int lane = threadIdx.x & 63;
-  const int grp = lane - q;              // first lane of this token's group
-  const int e0 = 64 * q;
-  constexpr int TPP = 256 / P;           // tokens per pass (T is a multiple)
-  const uint64_t valid = E - e0 >= 64 ? ~0ull : (E > e0 ? (1ull << (E - e0)) - 1 : 0ull);
-  for (int tl = threadIdx.x / P; tl < T; tl += TPP) {
-    const int64_t t = t0 + tl;
-    const bool live = t < L;
-    const float* row = logits + (live ? t : 0) * E;
-    float v[64];
-#pragma unroll
-    for (int j4 = 0; j4 < 16; ++j4) {
-      const int e = e0 + 4 * j4;
-      if (VEC) {
-        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (live && e < E) x = *reinterpret_cast<const float4*>(row + e);  // E % 4 == 0
-        v[4 * j4] = x.x; v[4 * j4 + 1] = x.y; v[4 * j4 + 2] = x.z; v[4 * j4 + 3] = x.w;
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[4 * j4 + u] = (live && e + u < E) ? row[e + u] : -INFINITY;
-      }
-    }
-    float b[KM];
-#pragma unroll
-    for (int i = 0; i < KM; ++i) b[i] = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-#pragma unroll
-      for (int i = KM - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], v[j]);
-      b[0] = fmaxf(b[0], v[j]);
-    }
-#pragma unroll
-    for (int o = 1; o < P; o <<= 1) {
-      float pb[KM];
-#pragma unroll
-      for (int i = 0; i < KM; ++i) pb[i] = __shfl_xor(b[i], o);
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-#pragma unroll
-        for (int i = KM - 1; i > 0; --i) b[i] = __builtin_amdgcn_fmed3f(b[i - 1], b[i], pb[j]);
-        b[0] = fmaxf(b[0], pb[j]);
-      }
-    }
-    float thr = b[0];
-#pragma unroll
-    for (int i = 1; i < KM; ++i) thr = (i == K - 1) ? b[i] : thr;
-
-    uint64_t ge = 0, gt = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      ge |= (uint64_t)(v[j] >= thr ? 1u : 0u) << j;
-      gt |= (uint64_t)(v[j] > thr ? 1u : 0u) << j;
-    }
-    ge &= valid;
-    gt &= valid;
-    // per-lane counts of the token's group, lane order = expert order
-    int cnt[P], tie[P];
-    const int mycnt = __builtin_popcountll(ge), mytie = __builtin_popcountll(ge & ~gt);
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-      cnt[r] = __shfl(mycnt, grp + r);
-      tie[r] = __shfl(mytie, grp + r);
-    }
-    int total = 0, above = 0;
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-      total += cnt[r];
-      above += r > q ? tie[r] : 0;
-    }
-    if (total > K) {  // drop surplus ties from the highest ids
-      int drop = min(max(total - K - above, 0), mytie);
-      uint64_t ties = ge & ~gt;
-      for (; drop > 0; --drop) {
-        const int hb = 63 - __builtin_clzll(ties);
-        ties &= ~(1ull << hb);
-        ge &= ~(1ull << hb);
-      }
-    } else if (total < K) {  // NaN logits only: fill with the lowest free ids
-      int freec[P];
-      const int myfree = __builtin_popcountll(valid & ~ge);
-#pragma unroll
-      for (int r = 0; r < P; ++r) freec[r] = __shfl(myfree, grp + r);
-      int below = 0;
-#pragma unroll
-      for (int r = 0; r < P; ++r) below += r < q ? freec[r] : 0;
-      int add = min(max(K - total - below, 0), myfree);
-      uint64_t fr = valid & ~ge;
-      for (; add > 0; --add) {
-        const uint64_t lo = fr & (~fr + 1);
-        fr &= ~lo;
-        ge |= lo;
-      }
-    }
-    const int kept = __builtin_popcountll(ge);
-    int base = 0;
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-      const int kr = __shfl(kept, grp + r);
-      base += r < q ? kr : 0;
-    }
-    if (live) {
-      const float vmax = b[0];
-      float ssum = 0.f;
-#pragma unroll
-      for (int i = 0; i < KM; ++i)
-        if (i < K) ssum += expf(b[i] - vmax);
-      const float inv = 1.0f / ssum;
-      uint64_t m = ge;
-      for (int slot = base; m != 0 && slot < K; ++slot) {
-        const int e = e0 + __builtin_ctzll(m);
-        m &= m - 1;
-        tei[t * K + slot] = e;
-        gates[t * K + slot] = expf(row[e] - vmax) * inv;
-        smap[e * T + tl] = (uint8_t)(slot + 1);
-      }
-    }
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int nv = T >> 4;
-  for (int e = wave; e < E; e += 4) {
-    int c = 0;
-    for (int i = lane; i < nv; i += 64) {
-      const uint4 w = smap_v[(e * T >> 4) + i];
-      *reinterpret_cast<uint4*>(map + (int64_t)e * Lpad + t0 + i * 16) = w;
-      c += nonzero_bytes(w.x) + nonzero_bytes(w.y) + nonzero_bytes(w.z) + nonzero_bytes(w.w);
-    }
-    c = wave_sum(c);
-    if (lane == 0) tilecnt[(int64_t)e * C + tile] = c;
-  }
-}
-
 // Step 1 for E <= 64: one thread per token with the token's logits in
 // registers (EV = E rounded up to a multiple of 4).  Top-K is K register
 // passes of an arg-max with ties to the lower id; no cross-lane traffic.
@@ -710,6 +550,352 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
     if (tid + u * 256 < nt) tim[t0 * K + tid + u * 256] = mv[u];
 }
 
+// ---------------------------------------------------------------- wide E
+// Bit-form map for 64 < E <= 64 P (P = 2, 4, 8 or 16 words of 64 experts per
+// token), K <= 8.  Same outputs as the E <= 64 kernels, per 64-token part:
+// each token's expert mask as P words (word q = experts 64q .. 64q+63), the
+// part's column ballot of every expert and the part's per-expert counts.
+//
+// Step 1.  One wavefront per workgroup routes one part in P rounds of 64 / P
+// tokens, P lanes per token: lane q of a token owns experts 64q .. 64q+63.
+// A round's logit rows (one contiguous run of 16 KB at most) are copied into
+// LDS with 1 KB direct-to-LDS transfers.  As in the E <= 64 router, each lane
+// reads its slice from LDS twice, 4 values at a time, starting at a
+// lane-dependent chunk (bank spreading), so few registers are live and many
+// workgroups share a CU: pass 1 keeps the slice's KM largest values (med3
+// network), the token's P lists are merged by a butterfly of shuffles, which
+// gives every lane of the token the token's K largest values and so the
+// K-th value thr; pass 2 marks the slice's experts >= thr.  Surplus marks can
+// only be ties with thr and are dropped from the highest expert ids (highest
+// lane first); a shortfall (NaN logits, outside the contract) is filled with
+// the lowest unmarked ids, so every token gets exactly K valid experts.
+// Slots follow the lanes' order, hence ascending expert id.  The part's
+// masks collect in LDS as [token][word]; after the last round one ballot per
+// expert and word gives the part's columns.
+template <int P, int KM, bool VEC>
+__global__ __launch_bounds__(64) void k1_route_wide_mask(
+    const float* __restrict__ logits, int64_t L, int E, int K, int64_t NP,
+    int32_t* __restrict__ tei, float* __restrict__ gates, uint64_t* __restrict__ tmask,
+    uint64_t* __restrict__ tcol, int32_t* __restrict__ partcnt) {
+  constexpr int TPR = 64 / P;                  // tokens per round
+  constexpr int STAGEB = 16384 + (VEC ? 0 : 1024);
+  __shared__ __attribute__((aligned(16))) char stage[STAGEB];
+  __shared__ uint64_t smask[64][P];
+  const int lane = threadIdx.x;
+  const int q = lane % P;               // slice of the token
+  const int i = lane / P;               // token of the round
+  const int grp = lane - q;             // first lane of the token
+  const int e0 = 64 * q;
+  const int ne = max(0, min(64, E - e0));  // experts in this lane's slice
+  const uint64_t valid = ne >= 64 ? ~0ull : ((1ull << ne) - 1);
+  const int rot = lane & 15;
+  const int rowb = 4 * E;
+  int64_t part;
+  {  // contiguous runs of parts per XCD: neighbouring parts' count words meet in one L2
+    const int64_t nb = gridDim.x, b = blockIdx.x, qq = nb >> 3, r = nb & 7, x = b & 7;
+    part = x * qq + (x < r ? x : r) + (b >> 3);
+  }
+  RouteSrc src;
+  {
+    const char* lbase = reinterpret_cast<const char*>(logits);
+    src.mis = (int64_t)(reinterpret_cast<uintptr_t>(lbase) & 15);  // 0 when VEC
+    src.abase = lbase - src.mis;
+    src.end16 = (src.mis + L * rowb + 15) & ~(int64_t)15;
+  }
+  for (int rd = 0; rd < P; ++rd) {
+    const int64_t tr0 = part * 64 + (int64_t)rd * TPR;   // first token of the round
+    const int64_t first = src.mis + tr0 * rowb;
+    const int64_t first16 = first & ~(int64_t)15;
+    const int delta = (int)(first - first16);
+    const int nq = tr0 < L ? (int)((delta + (int64_t)TPR * rowb + 1023) >> 10) : 0;
+    // the previous round's LDS reads are done before its stage is rewritten
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int c = 0; c < nq; ++c) {
+      const int64_t off = first16 + (int64_t)c * 1024 + lane * 16;
+      const char* g = src.abase + (off + 16 <= src.end16 ? off : 0);
+      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(stage + c * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+
+    const int64_t t = tr0 + i;
+    const bool live = t < L;
+    const float* row = reinterpret_cast<const float*>(stage + delta + (int64_t)i * rowb) + e0;
+    auto chunk = [&](int c, float (&v)[4]) {
+      if (VEC && 4 * c + 4 <= ne) {
+        const float4 x = reinterpret_cast<const float4*>(row)[c];
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = 4 * c + u < ne ? row[4 * c + u] : -INFINITY;
+      }
+    };
+    float b[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) b[k] = -INFINITY;
+    // (not unrolled: four values live at a time keep the register count low)
+#pragma unroll 2
+    for (int j = 0; j < 16; ++j) {
+      float v[4];
+      chunk((j + rot) & 15, v);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int k = KM - 1; k > 0; --k) b[k] = __builtin_amdgcn_fmed3f(b[k - 1], b[k], v[u]);
+        b[0] = fmaxf(b[0], v[u]);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) {
+      float pb[KM];
+#pragma unroll
+      for (int k = 0; k < KM; ++k) pb[k] = __shfl_xor(b[k], o);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+#pragma unroll
+        for (int k = KM - 1; k > 0; --k) b[k] = __builtin_amdgcn_fmed3f(b[k - 1], b[k], pb[j]);
+        b[0] = fmaxf(b[0], pb[j]);
+      }
+    }
+    float thr = b[0];
+#pragma unroll
+    for (int k = 1; k < KM; ++k) thr = (k == K - 1) ? b[k] : thr;
+
+    uint64_t ge = 0, gt = 0;
+#pragma unroll 2
+    for (int j = 0; j < 16; ++j) {
+      const int c = (j + rot) & 15;
+      float v[4];
+      chunk(c, v);
+      const uint32_t g4 = (v[0] >= thr ? 1u : 0u) | (v[1] >= thr ? 2u : 0u) |
+                          (v[2] >= thr ? 4u : 0u) | (v[3] >= thr ? 8u : 0u);
+      const uint32_t t4 = (v[0] > thr ? 1u : 0u) | (v[1] > thr ? 2u : 0u) |
+                          (v[2] > thr ? 4u : 0u) | (v[3] > thr ? 8u : 0u);
+      ge |= (uint64_t)g4 << (4 * c);
+      gt |= (uint64_t)t4 << (4 * c);
+    }
+    ge &= valid;
+    gt &= valid;
+    int cnt[P], tie[P];
+    const int mycnt = __builtin_popcountll(ge), mytie = __builtin_popcountll(ge & ~gt);
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      cnt[r] = __shfl(mycnt, grp + r);
+      tie[r] = __shfl(mytie, grp + r);
+    }
+    int total = 0, above = 0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      total += cnt[r];
+      above += r > q ? tie[r] : 0;
+    }
+    if (total > K) {  // drop surplus ties from the highest ids
+      int drop = min(max(total - K - above, 0), mytie);
+      uint64_t ties = ge & ~gt;
+      for (; drop > 0; --drop) {
+        const int hb = 63 - __builtin_clzll(ties);
+        ties &= ~(1ull << hb);
+        ge &= ~(1ull << hb);
+      }
+    } else if (total < K) {  // NaN logits only: fill with the lowest free ids
+      const int myfree = __builtin_popcountll(valid & ~ge);
+      int below = 0;
+#pragma unroll
+      for (int r = 0; r < P; ++r) {
+        const int fr = __shfl(myfree, grp + r);
+        below += r < q ? fr : 0;
+      }
+      int add = min(max(K - total - below, 0), myfree);
+      uint64_t fr = valid & ~ge;
+      for (; add > 0; --add) {
+        const uint64_t lo = fr & (~fr + 1);
+        fr &= ~lo;
+        ge |= lo;
+      }
+    }
+    const int kept = __builtin_popcountll(ge);
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      const int kr = __shfl(kept, grp + r);
+      base += r < q ? kr : 0;
+    }
+    const uint64_t m = live ? ge : 0ull;
+    smask[rd * TPR + i][q] = m;
+    if (live) {
+      tmask[t * P + q] = m;
+      const float vmax = b[0];
+      float ssum = 0.f;
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (k < K) ssum += expf(b[k] - vmax);
+      const float inv = 1.0f / ssum;
+      uint64_t mm = m;
+      for (int slot = base; mm != 0 && slot < K; ++slot) {
+        const int j = __builtin_ctzll(mm);
+        mm &= mm - 1;
+        tei[t * K + slot] = e0 + j;
+        gates[t * K + slot] = expf(row[j] - vmax) * inv;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // columns: word qw of the part's 64 tokens -> one ballot per expert 64 qw + lane
+  for (int qw = 0; qw < P; ++qw) {
+    const uint64_t mw = smask[lane][qw];
+    uint32_t col_lo = 0, col_hi = 0;
+    BallotColumns<0, 64>::run(mw, col_lo, col_hi);
+    const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+    const int e = 64 * qw + lane;
+    if (e < E) {
+      tcol[part * E + e] = mycol;
+      partcnt[(int64_t)e * NP + part] = __popcll(mycol);
+    }
+  }
+}
+
+// Step 3 for the wide bit form (E <= 64 W): one workgroup per 256-token tile
+// (four parts, one token per thread).  As in the E <= 64 scatter, a route's
+// position is the expert's segment start plus the tile base from the scan,
+// plus the part's running base inside the tile, plus the set bits of the
+// part's column below the token's lane; the tile's entries are staged in
+// LDS by expert and written out run by run, and the tile's token_index_map
+// rows leave as one contiguous run.  Expert-indexed work (segment starts,
+// running bases, run starts) is spread over the 256 threads, EPT
+// consecutive experts each.
+template <int W>
+__global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restrict__ tmask,
+                                                       const uint64_t* __restrict__ tcol,
+                                                       int64_t L, int E, int K, int NU,
+                                                       const int32_t* __restrict__ unitbase,
+                                                       const int32_t* __restrict__ total,
+                                                       int32_t* __restrict__ eti,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ tim) {
+  constexpr int EM = 64 * W;
+  constexpr int EPT = (EM + 255) / 256;  // experts per thread
+  constexpr int MAXE = 256 * 8;          // entries of one tile (K <= 8)
+  __shared__ int s_off[EM + 1];
+  __shared__ int scratch[4];
+  __shared__ uint64_t s_col[4][EM];
+  __shared__ int s_base[4][EM];
+  __shared__ int s_run[EM + 1];
+  __shared__ int s_tok[MAXE];
+  __shared__ int s_pos[MAXE];
+  __shared__ int s_tim[MAXE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int tile;
+  {
+    const int nb = gridDim.x, b = blockIdx.x, q = nb >> 3, r = nb & 7, x = b & 7;
+    tile = x * q + (x < r ? x : r) + (b >> 3);
+  }
+  const int64_t t = (int64_t)tile * 256 + tid;
+  uint64_t mk[W];
+#pragma unroll
+  for (int qw = 0; qw < W; ++qw) mk[qw] = t < L ? tmask[t * W + qw] : 0ull;
+  for (int f = tid; f < 4 * EM; f += 256) {
+    const int w = f / EM, e = f % EM;
+    const int64_t part = (int64_t)tile * 4 + w;
+    s_col[w][e] = (e < E && part * 64 < L) ? tcol[part * E + e] : 0ull;
+  }
+  // expert segment starts: exclusive scan of the totals
+  int tv[EPT], ub[EPT];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    tv[j] = e < E ? total[e] : 0;
+    ub[j] = e < E ? unitbase[(int64_t)e * NU + tile] : 0;
+    sum += tv[j];
+  }
+  int tot;
+  int ex = block256_incl_scan(sum, scratch, &tot) - sum;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    if (e < E) s_off[e] = ex;
+    ex += tv[j];
+  }
+  if (tid == 0) s_off[E] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += 256) offsets[e] = s_off[e];
+  // running bases of the four parts and the tile's count of each expert
+  int n[EPT];
+  int nsum = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    n[j] = 0;
+    if (e < E) {
+      int run = s_off[e] + ub[j];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s_base[w][e] = run;
+        const int c = __popcll(s_col[w][e]);
+        run += c;
+        n[j] += c;
+      }
+    }
+    nsum += n[j];
+  }
+  int ntot;
+  int rx = block256_incl_scan(nsum, scratch, &ntot) - nsum;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    if (e < E) s_run[e] = rx;
+    rx += n[j];
+  }
+  if (tid == 0) s_run[E] = ntot;
+  __syncthreads();
+  if (t < L) {
+    int qw = 0;
+    for (int k = 0; k < K; ++k) {
+      int pos = -1;  // (masks with fewer than K bits leave -1)
+      while (qw < W && mk[qw] == 0) ++qw;
+      if (qw < W) {
+        const int e = 64 * qw + lowest_bit(mk[qw]);
+        mk[qw] &= mk[qw] - 1;
+        const uint64_t ce = s_col[wave][e];
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(ce >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)ce, 0));
+        pos = s_base[wave][e] + below;
+        const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
+        if (lp < MAXE) {  // always true when the masks hold K bits each
+          s_tok[lp] = (int32_t)t;
+          s_pos[lp] = pos;
+        }
+      }
+      s_tim[tid * K + k] = pos;
+    }
+  }
+  __syncthreads();
+  constexpr int NJ = MAXE / 256;
+  const int nrun = min(s_run[E], MAXE);
+  const int64_t R = L * K;
+  int pv[NJ], tk[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) {
+    const int j = min(tid + u * 256, MAXE - 1);
+    pv[u] = s_pos[j];
+    tk[u] = s_tok[j];
+  }
+#pragma unroll
+  for (int u = 0; u < NJ; ++u)  // pos < R always holds when the masks hold K bits each
+    if (tid + u * 256 < nrun && pv[u] >= 0 && pv[u] < R) eti[pv[u]] = tk[u];
+  const int64_t t0 = (int64_t)tile * 256;
+  const int nt = (int)min((int64_t)256, L - t0) * K;
+  int mv[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) mv[u] = s_tim[min(tid + u * 256, MAXE - 1)];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u)
+    if (tid + u * 256 < nt) tim[t0 * K + tid + u * 256] = mv[u];
+}
+
 // Exclusive scan of each row of a [rows][C] count table (one workgroup per
 // row): base[r][c] = r * row_offset + sum of counts[r][0..c).  total[r] gets
 // the row sum when total is not null.  With G > 1 the input rows hold G
@@ -847,13 +1033,23 @@ void launch_seg_scan(const int32_t* cnt, int rows, int C, int64_t row_offset, in
   hipLaunchKernelGGL(seg_scan<1>, dim3(rows), dim3(256), 0, s, cnt, C, row_offset, base, total);
 }
 
-// The streaming kernels (bit-mask map, 256-token tiles) serve E <= 64 and
-// K <= 8; larger E or K use the byte map with 256..1024-token tiles.
-static bool stream_path(int E, int K) { return E <= 64 && K <= 8; }
+// The bit-form kernels (256-token tiles) serve E <= 1024 and K <= 8: one
+// 64-bit mask word per token for E <= 64, P (a power of two, 2..16) words
+// for larger E.  K > 8 (E <= 256) uses the byte map with 256..1024-token
+// tiles.
+static bool stream_path(int E, int K) { return E <= 1024 && K <= 8; }
+
+static int mask_words(int E) {
+  if (E <= 64) return 1;
+  int P = 2;
+  while (64 * P < E) P <<= 1;
+  return P;
+}
 
 DispatchPlan plan_dispatch(int64_t L, int E, int K) {
   DispatchPlan p;
   p.stream = stream_path(E, K);
+  p.W = p.stream ? mask_words(E) : 0;
   int T;
   if (p.stream) {
     T = 256;
@@ -870,14 +1066,14 @@ DispatchPlan plan_dispatch(int64_t L, int E, int K) {
   // every part of every 256-token tile is routed (parts past L write zero
   // counts), so the grouped scan reads only written entries
   p.NP = p.stream ? (int64_t)4 * p.C : 0;
-  // map: one 64-bit expert mask per token (stream) or the [E][Lpad] byte map
-  const size_t map_bytes = p.stream ? (size_t)8 * p.Lpad : (size_t)E * p.Lpad;
+  // map: W 64-bit expert mask words per token (bit form) or the [E][Lpad] byte map
+  const size_t map_bytes = p.stream ? (size_t)8 * p.W * p.Lpad : (size_t)E * p.Lpad;
   size_t o = 0;
   p.off_map = o;   o = align_up(o + map_bytes, 256);
   p.off_col = o;   o = align_up(o + (p.stream ? (size_t)8 * E * (p.Lpad / 64) : 0), 256);
   p.off_cnt = o;   o = align_up(o + (size_t)E * (p.stream ? 4 * p.C : p.C) * 4, 256);
   p.off_base = o;  o = align_up(o + (size_t)E * p.C * 4, 256);
-  p.off_total = o; o = align_up(o + 256 * 4, 256);
+  p.off_total = o; o = align_up(o + (size_t)(E > 256 ? E : 256) * 4, 256);
   p.bytes = o;
   return p;
 }
@@ -931,16 +1127,12 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
         K1M_K(16)
       } else if (E <= 32) {
         K1M_K(32)
-      } else {
+      } else if (E <= 64) {
         K1M_K(64)
-      }
-#undef K1M_K
-#undef K1M
-    } else if (E <= 256 && K <= 8 && pl.T == 256) {
-      const size_t sh = (size_t)E * pl.T;
+      } else {
 #define K1W(PV, KV, VV)                                                                         \
-  hipLaunchKernelGGL((k1_route_wide<PV, KV, VV>), dim3(pl.C), dim3(256), sh, s, logits, L, E, K, \
-                     pl.T, pl.C, pl.Lpad, tei, gates, map, cnt)
+  hipLaunchKernelGGL((k1_route_wide_mask<PV, KV, VV>), dim3(pl.NP), dim3(64), 0, s, logits, L, E, \
+                     K, pl.NP, tei, gates, tmask, tcol, cnt)
 #define K1W_K(PV)                                                                               \
   if (!rows_ok) {                                                                               \
     K1W(PV, 8, false);                                                                          \
@@ -956,13 +1148,17 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
       default: K1W(PV, 8, true); break;                                                         \
     }                                                                                           \
   }
-      if (E <= 128) {
-        K1W_K(2)
-      } else {
-        K1W_K(4)
-      }
+        switch (pl.W) {
+          case 2: K1W_K(2) break;
+          case 4: K1W_K(4) break;
+          case 8: K1W_K(8) break;
+          default: K1W_K(16) break;
+        }
 #undef K1W_K
 #undef K1W
+      }
+#undef K1M_K
+#undef K1M
     } else if (rows_ok && E <= 64) {
       const size_t sh = (size_t)E * pl.T;
 #define MOE_K1R(EVV)                                                                            \
@@ -991,11 +1187,23 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
   }
   {
     LaunchTimer lt("dispatch_scatter", s);
-    if (pl.stream)
-      hipLaunchKernelGGL(k3_scatter_mask<4>, dim3(pl.C), dim3(256), 0, s,
-                         reinterpret_cast<const uint64_t*>(ws + pl.off_map),
-                         reinterpret_cast<const uint64_t*>(ws + pl.off_col), L, E, K, pl.C, base,
-                         total, eti, offsets, tim);
+    const uint64_t* tmask = reinterpret_cast<const uint64_t*>(ws + pl.off_map);
+    const uint64_t* tcol = reinterpret_cast<const uint64_t*>(ws + pl.off_col);
+#define K3W(WV)                                                                                 \
+  hipLaunchKernelGGL(k3_scatter_wide<WV>, dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K, pl.C, \
+                     base, total, eti, offsets, tim)
+    if (pl.stream && pl.W == 1)
+      hipLaunchKernelGGL(k3_scatter_mask<4>, dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K,
+                         pl.C, base, total, eti, offsets, tim);
+    else if (pl.stream && pl.W == 2)
+      K3W(2);
+    else if (pl.stream && pl.W == 4)
+      K3W(4);
+    else if (pl.stream && pl.W == 8)
+      K3W(8);
+    else if (pl.stream)
+      K3W(16);
+#undef K3W
     else
       hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
                          base, total, eti, offsets, tim);

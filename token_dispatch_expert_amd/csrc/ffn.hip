@@ -45,6 +45,7 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -652,21 +653,35 @@ __global__ __launch_bounds__(256) void transpose_weights(const T* __restrict__ W
 
 // Split each of G segment lists (seg[g*(E+1) + e] .. seg[g*(E+1) + e + 1])
 // into row tiles of at most TBM rows.  desc[g][i] = {e, begin, end, 0} or
-// {-1, 0, 0, 0} past the last tile.
+// {-1, 0, 0, 0} past the last tile.  E <= 1024: each thread counts the tiles
+// of four consecutive experts.
+constexpr int kMaxExperts = 1024;
 __global__ __launch_bounds__(256) void tile_table(const int32_t* __restrict__ seg, int E,
                                                   int64_t max_tiles, int4* __restrict__ desc,
                                                   uint4* __restrict__ zero_page) {
-  __shared__ int s_start[257];
+  constexpr int EPT = kMaxExperts / 256;
+  __shared__ int s_start[kMaxExperts + 1];
   __shared__ int scratch[4];
   if (zero_page != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 16)
     zero_page[threadIdx.x] = make_uint4(0, 0, 0, 0);
   const int grp = blockIdx.y;
   const int32_t* off = seg + (int64_t)grp * (E + 1);
   const int tid = threadIdx.x;
-  const int n = tid < E ? (off[tid + 1] - off[tid] + TBM - 1) / TBM : 0;
+  int n[EPT], sum = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    n[j] = e < E ? (off[e + 1] - off[e] + TBM - 1) / TBM : 0;
+    sum += n[j];
+  }
   int tot;
-  const int inc = block256_incl_scan(n, scratch, &tot);
-  if (tid < E) s_start[tid] = inc - n;
+  int ex = block256_incl_scan(sum, scratch, &tot) - sum;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    if (e < E) s_start[e] = ex;
+    ex += n[j];
+  }
   if (tid == 0) s_start[E] = tot;
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 256 + tid;
@@ -1267,22 +1282,24 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
     b1_epilogue<T, DUAL, ROUTER, false>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
 }
 
-// Router gradient, one workgroup per 64 tokens.  Every thread first takes
-// routes (t, k) of the block: dg_k = <dy[t], O[tim[t, k]]> is the sum of the
-// route's partials in ascending tile order, parked at the token's row in LDS
-// under its expert.  Then lane t of wavefront 0 forms the softmax backward
-// over the selected logits, dz_k = g_k (dg_k - sum_j g_j dg_j), sum in
-// ascending k, in place; then the workgroup writes the 64 full rows of
-// dlogits (zeros for experts not chosen).
+// Router gradient, one workgroup per TB tokens (TB * E <= 16384: 64 tokens
+// up to 256 experts, fewer beyond).  Every thread first takes routes (t, k)
+// of the block: dg_k = <dy[t], O[tim[t, k]]> is the sum of the route's
+// partials in ascending tile order, parked at the token's row in LDS under
+// its expert.  Then lane t of wavefront 0 forms the softmax backward over
+// the selected logits, dz_k = g_k (dg_k - sum_j g_j dg_j), sum in ascending
+// k, in place; then the workgroup writes the TB full rows of dlogits (zeros
+// for experts not chosen).
+constexpr int kRouterRows = 16384;  // floats of LDS: TB rows of E
 __global__ __launch_bounds__(256) void router_grad(const int32_t* __restrict__ tei,
                                                    const int32_t* __restrict__ tim,
                                                    const float* __restrict__ gates,
                                                    const float* __restrict__ dgp, int nN,
-                                                   int64_t L, int E, int K,
+                                                   int64_t L, int E, int K, int TB,
                                                    float* __restrict__ dz) {
-  __shared__ float s_rows[64 * 256];
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const int nrow = (int)min<int64_t>(64, L - t0);
+  __shared__ float s_rows[kRouterRows];
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int nrow = (int)min<int64_t>(TB, L - t0);
   for (int i = threadIdx.x; i < nrow * E; i += 256) s_rows[i] = 0.f;
   __syncthreads();
   const int nr = nrow * K;  // routes of the block: rows t0 .. t0 + nrow of tim, tei
@@ -1657,8 +1674,9 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   }
   if (dlogits != nullptr) {
     LaunchTimer lt("router_grad", s);
-    hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, 64)), dim3(256), 0, s, tei, tim,
-                       gates, dgp, nNh, dm.L, dm.E, dm.K, dlogits);
+    const int TB = std::min(64, kRouterRows / dm.E);
+    hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, TB)), dim3(256), 0, s, tei, tim,
+                       gates, dgp, nNh, dm.L, dm.E, dm.K, TB, dlogits);
   }
   {
     LaunchTimer lt("ffn_b0_dw2", s);

@@ -27,7 +27,8 @@ struct DispatchPlan {
   int T;          // tokens per tile
   int C;          // tiles
   int64_t Lpad;   // C * T (row length of the token-expert map)
-  bool stream;    // bit-mask map (E <= 64, K <= 8)
+  bool stream;    // bit-form map (E <= 1024, K <= 8)
+  int W;          // 64-bit mask words per token (bit form)
   int64_t NP;     // 64-token parts of the streaming router (per-part counts)
   size_t off_map, off_col, off_cnt, off_base, off_total, bytes;
 };
