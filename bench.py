@@ -218,31 +218,47 @@ def _emit(d):
     print(json.dumps(d), flush=True)
 
 
-def study_memory(cfg, seed, dev):
-    """Device memory of one layer step: what the method keeps between forward
-    and backward (A, B), the transient buffers, the measured peak (torch's
-    allocator holds every buffer), and, for scale, the two (L*K, d) buffers a
-    materialising layer keeps (routed copy of x, per-route expert output)."""
+def study_memory(cfg, seed, dev, steps=3):
+    """Device memory and step time of one layer step, with G kept between
+    the two GEMMs of each pass (default) and with G formed at operand load
+    (MOE_FLAG_RECOMPUTE_G): what the method keeps between forward and
+    backward (A, B), the transient buffers, the measured peak (torch's
+    allocator holds every buffer), and, for scale, the two (L*K, d) buffers
+    a materialising layer keeps (routed copy of x, per-route expert output)."""
     es = 2 if cfg.dtype == W.BF16 else 4
-    torch.zeros(1, device=dev)
-    torch.cuda.synchronize(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
     inp = W.make_inputs(cfg, seed, dev)
     torch.cuda.synchronize()
-    m_inputs = torch.cuda.memory_allocated(dev)
-    buf = MoELayerBuffers(cfg, dev)
-    torch.cuda.synchronize()
-    m_buffers = torch.cuda.memory_allocated(dev)
-    buf.step(inp)
-    torch.cuda.synchronize()
-    _emit({"study": "memory", "workload": cfg.name,
-           "checkpoint_bytes": cfg.R * cfg.h * (2 if cfg.act == W.SWIGLU else 1) * es,
-           "transient_G_bytes": cfg.R * cfg.h * es,
-           "workspace_bytes": int(buf.ws.numel()),
-           "inputs_bytes": int(m_inputs),
-           "layer_buffers_bytes": int(m_buffers - m_inputs),
-           "peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
-           "materialising_layer_extra_bytes": 2 * cfg.R * cfg.d * es})
+    for recompute in (False, True):
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        m_inputs = torch.cuda.memory_allocated(dev)
+        buf = MoELayerBuffers(cfg, dev, recompute_g=recompute)
+        torch.cuda.synchronize()
+        m_buffers = torch.cuda.memory_allocated(dev)
+        buf.step(inp)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev)
+        B.profile_reset()
+        B.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            buf.step(inp)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        B.profile_enable(False)
+        st = B.profile_read()
+        _emit({"study": "memory", "workload": cfg.name,
+               "mode": "G formed at operand load" if recompute else "G kept",
+               "checkpoint_bytes": cfg.R * cfg.h * (2 if cfg.act == W.SWIGLU else 1) * es,
+               "transient_G_bytes": 0 if recompute else cfg.R * cfg.h * es,
+               "workspace_bytes": int(buf.ws.numel()),
+               "inputs_bytes": int(m_inputs),
+               "layer_buffers_bytes": int(m_buffers - m_inputs),
+               "peak_allocated_bytes": int(peak),
+               "ms_per_step": ms,
+               "kernels_ms": {k: v[1] / steps for k, v in st.items()},
+               "materialising_layer_extra_bytes": 2 * cfg.R * cfg.d * es})
+        del buf
 
 
 def study_dispatch_e(cfg, seed, dev, reps=20):
@@ -350,6 +366,8 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute-g", action="store_true",
+                    help="MOE_FLAG_RECOMPUTE_G: no G buffer; the second GEMMs form G from A, B")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scale reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -391,7 +409,7 @@ def main():
         return
     log(f"[bench] {cfg.name}: generating inputs on {torch.cuda.get_device_name(0)}")
     inp = W.make_inputs(cfg, seed, dev)
-    buf = MoELayerBuffers(cfg, dev)
+    buf = MoELayerBuffers(cfg, dev, recompute_g=args.recompute_g)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -446,7 +464,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "L": cfg.L, "d": cfg.d, "h": cfg.h, "E": cfg.E,
                    "K": cfg.K, "act": "swiglu" if cfg.act == W.SWIGLU else "silu",
-                   "seed": seed, "parallelism": "none (1 GPU)"},
+                   "seed": seed, "parallelism": "none (1 GPU)",
+                   "g_buffer": "none (G formed at operand load)" if args.recompute_g else "kept"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "flops_per_launch": kflops[dom],

@@ -73,6 +73,18 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
  * (W1 = gate projection, W3 = up projection, W2 = down projection.) */
 enum { MOE_SILU = 0, MOE_SWIGLU = 1 };
 
+/* Flags of moe_shape.flags (0 = none).
+ *   MOE_FLAG_RECOMPUTE_G: keep no copy of G = SiLU(A) [* B] between the
+ *     two GEMMs of either pass.  The forward stores only A and B; its
+ *     second GEMM forms G from A and B as it loads its operand, and the
+ *     backward forms gate * G the same way for dW2 (before dA, dB replace
+ *     A, B).  The workspace then holds no [L*K, h] buffer (half the
+ *     checkpoint's size for SwiGLU, all of it for SiLU) at the price of
+ *     reading A and B instead of G.  Results agree with the default within
+ *     the bf16 rounding of G (G is formed from the stored A, B instead of
+ *     their float32 accumulators). */
+enum { MOE_FLAG_RECOMPUTE_G = 1 };
+
 typedef struct moe_shape {
   int64_t L;     /* tokens                                  */
   int32_t d;     /* model width                             */
@@ -81,6 +93,7 @@ typedef struct moe_shape {
   int32_t K;     /* experts per token (top-K)               */
   int32_t dtype; /* MOE_F32 or MOE_BF16                     */
   int32_t act;   /* MOE_SILU or MOE_SWIGLU                  */
+  int32_t flags; /* MOE_FLAG_* bits, 0 for none (FFN calls)  */
 } moe_shape;
 
 /*

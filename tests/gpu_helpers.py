@@ -91,10 +91,10 @@ def full_inputs_host(inp):
     return {k: host(v) if k != "logits" else v.cpu().numpy() for k, v in inp.items()}
 
 
-def run_full_parity(cfg, seed, device, inp=None, check_determinism=False):
+def run_full_parity(cfg, seed, device, inp=None, check_determinism=False, recompute_g=False):
     """Whole-tensor parity for shapes the oracle runs in seconds."""
     inp = inp or W.make_inputs(cfg, seed, device)
-    buf = MoELayerBuffers(cfg, device, router_grad=True)
+    buf = MoELayerBuffers(cfg, device, router_grad=True, recompute_g=recompute_g)
     h_in = full_inputs_host(inp)
     ref = oracle_dispatch(h_in["logits"], cfg)
     buf.build(inp["logits"])
@@ -151,16 +151,16 @@ def _dw_columns_for(n_e, d, h, rng, budget=4e11):
     return np.unique(cols)
 
 
-def run_sampled_parity(cfg, seed, device, n_tokens=4096):
+def run_sampled_parity(cfg, seed, device, n_tokens=4096, recompute_g=False):
     """Parity at full size on outputs the oracle computes from a subset of
     rows: indices in full; y, dx, dlogits and the A/B rows of n_tokens
     seeded tokens (plus the first and the last); dW1/dW3/dW2 of the
     heaviest, the lightest non-empty and one random other expert (whole
     matrices where the oracle runs them in seconds, else a column subset
     covering whole tiles), and exact zeros for every empty expert."""
-    say(f"  sampled parity {cfg.name} seed {seed}")
+    say(f"  sampled parity {cfg.name} seed {seed}" + (" (G formed at operand load)" if recompute_g else ""))
     inp = W.make_inputs(cfg, seed, device)
-    buf = MoELayerBuffers(cfg, device, router_grad=True)
+    buf = MoELayerBuffers(cfg, device, router_grad=True, recompute_g=recompute_g)
     logits = inp["logits"].cpu().numpy()
     ref = oracle_dispatch(logits, cfg)
     buf.build(inp["logits"])

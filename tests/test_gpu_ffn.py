@@ -136,3 +136,38 @@ def test_outputs_leave_neighbours_untouched():
     torch.cuda.synchronize()
     for s in (ystore, dxstore, dzstore):
         assert torch.all(s[:pad] == 7.0) and torch.all(s[-pad:] == 7.0)
+
+
+# MOE_FLAG_RECOMPUTE_G: no G buffer; the down-projection and dW2 form
+# G = SiLU(A) [* B] (times the gate for dW2) from the checkpoint at operand
+# load, and dW2 runs before the dG kernel replaces A and B.
+RECOMP = [
+    (1000, 256, 384, 8, 2, SWIGLU, W.BF16),
+    (777, 136, 200, 6, 3, SWIGLU, W.BF16),
+    (640, 192, 256, 4, 2, SILU, W.BF16),
+    (300, 72, 96, 5, 2, SWIGLU, W.F32),
+    (400, 128, 64, 4, 4, SILU, W.F32),
+    (1100, 520, 648, 8, 3, SWIGLU, W.BF16),
+    (700, 2048, 384, 4, 2, SWIGLU, W.BF16),
+    (100, 64, 64, 256, 1, SWIGLU, W.BF16),
+    (64, 8, 8, 4, 2, SWIGLU, W.BF16),
+]
+
+
+@pytest.mark.parametrize("L,d,h,E,K,act,dt", RECOMP,
+                         ids=[f"L{a}-d{b}-h{c}-E{e}-K{k}-{'glu' if t else 'silu'}-{'bf16' if u else 'f32'}"
+                              for a, b, c, e, k, t, u in RECOMP])
+def test_small_full_recompute_g(L, d, h, E, K, act, dt):
+    cfg = W.small_config(L, d, h, E, K, act, dt)
+    say(f"  {cfg.name}, G formed at operand load")
+    run_full_parity(cfg, 11, require_gpu(), recompute_g=True)
+
+
+@pytest.mark.parametrize("ci", [1, 2])
+def test_configs_full_recompute_g(ci):
+    say(f"  config {ci}, whole tensors, G formed at operand load")
+    run_full_parity(W.CONFIGS[ci], ci, require_gpu(), recompute_g=True)
+
+
+def test_largest_config_sampled_recompute_g():
+    run_sampled_parity(W.CONFIGS[5], 5, require_gpu(), recompute_g=True)

@@ -22,12 +22,13 @@ pytestmark = pytest.mark.gpu
 SLACK = 2 << 20
 
 
+@pytest.mark.parametrize("recompute_g", [False, True], ids=["keep_g", "recompute_g"])
 @pytest.mark.parametrize("cfg", [
     W.small_config(8192, 512, 1024, 16, 4, W.SWIGLU, W.BF16),
     W.small_config(5000, 256, 768, 8, 2, W.SILU, W.BF16),
     W.CONFIGS[3],
 ], ids=lambda c: c.name)
-def test_step_allocates_only_declared_buffers(cfg):
+def test_step_allocates_only_declared_buffers(cfg, recompute_g):
     dev = require_gpu()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -35,7 +36,7 @@ def test_step_allocates_only_declared_buffers(cfg):
     inp = W.make_inputs(cfg, 7, dev)
     torch.cuda.synchronize()
     m_inputs = torch.cuda.memory_allocated(dev) - base
-    buf = MoELayerBuffers(cfg, dev, router_grad=True)
+    buf = MoELayerBuffers(cfg, dev, router_grad=True, recompute_g=recompute_g)
     torch.cuda.synchronize()
     m_layer = torch.cuda.memory_allocated(dev) - base - m_inputs
 

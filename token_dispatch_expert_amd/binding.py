@@ -23,6 +23,7 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_SILU = 0
 MOE_SWIGLU = 1
+MOE_FLAG_RECOMPUTE_G = 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_dispatch.so")
 
@@ -41,7 +42,7 @@ EXPORTED = (
 class Shape(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int64), ("d", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("act", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class KernelStat(ctypes.Structure):
@@ -160,8 +161,8 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def make_shape(L, d, h, E, K, dtype=MOE_BF16, act=MOE_SWIGLU) -> Shape:
-    return Shape(int(L), int(d), int(h), int(E), int(K), int(dtype), int(act))
+def make_shape(L, d, h, E, K, dtype=MOE_BF16, act=MOE_SWIGLU, flags=0) -> Shape:
+    return Shape(int(L), int(d), int(h), int(E), int(K), int(dtype), int(act), int(flags))
 
 
 def _run(fn, shape, args, ws, stream, device):

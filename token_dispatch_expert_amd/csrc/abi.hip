@@ -56,6 +56,8 @@ int check_ffn_shape(const moe_shape* s) {
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
   if (s->act != MOE_SILU && s->act != MOE_SWIGLU)
     return fail(MOE_ERR_INVALID_ARG, "unknown act %d", s->act);
+  if ((s->flags & ~MOE_FLAG_RECOMPUTE_G) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)s->flags);
   if (s->d < 1 || s->h < 1) return fail(MOE_ERR_INVALID_ARG, "d and h must be >= 1 (d=%d, h=%d)", s->d, s->h);
   if (s->d % 8 != 0 || s->h % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "d and h must be multiples of 8 (d=%d, h=%d)", s->d, s->h);
@@ -107,6 +109,7 @@ int check_ws(void* ws, size_t* ws_bytes, size_t need, bool* query) {
 moe::FfnDims dims_of(const moe_shape* s) {
   moe::FfnDims d;
   d.L = s->L; d.d = s->d; d.h = s->h; d.E = s->E; d.K = s->K; d.dtype = s->dtype; d.act = s->act;
+  d.recompute_g = (s->flags & MOE_FLAG_RECOMPUTE_G) != 0;
   return d;
 }
 

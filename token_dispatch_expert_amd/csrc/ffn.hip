@@ -784,6 +784,181 @@ __global__ __launch_bounds__(256) void list_bounds(const int32_t* __restrict__ l
   pe_off[i] = (int32_t)(k * L + lo);
 }
 
+// ------------------------------------------------------------------ G at operand load
+// With G not kept (MOE_FLAG_RECOMPUTE_G) the second-layer GEMMs form their
+// operand G = SiLU(A) [* B] (and gate * G for dW2) from the checkpoint as
+// they load it: A and B arrive in registers, G is computed in float32 and
+// rounded once, and the result is written to LDS exactly where a copy of G
+// would have landed.  These loaders use the register path of the main loop
+// (loads in flight during the MFMAs of the current k-tile, LDS writes after
+// them).
+
+// 16 bytes of A and B (8 bf16 or 4 float32 each) -> 16 bytes of gate * G.
+template <typename T>
+__device__ __forceinline__ uint4 glu16(uint4 a, uint4 b, bool dual, float gate);
+template <>
+__device__ __forceinline__ uint4 glu16<bf16_t>(uint4 a, uint4 b, bool dual, float gate) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a0 = __uint_as_float(wa[k] << 16), a1 = __uint_as_float(wa[k] & 0xffff0000u);
+    float g0 = silu_of<bf16_t>(a0), g1 = silu_of<bf16_t>(a1);
+    if (dual) {
+      g0 *= __uint_as_float(wb[k] << 16);
+      g1 *= __uint_as_float(wb[k] & 0xffff0000u);
+    }
+    o[k] = (uint32_t)f2bf(gate * g0) | ((uint32_t)f2bf(gate * g1) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+template <>
+__device__ __forceinline__ uint4 glu16<float>(uint4 a, uint4 b, bool dual, float gate) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float g = silu_of<float>(__uint_as_float(wa[k]));
+    if (dual) g *= __uint_as_float(wb[k]);
+    o[k] = __float_as_uint(gate * g);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Rows of G (k contiguous) for the down-projection: the KLoaderD layout,
+// filled from registers.  Row r of the tile is route list[rb + r]; A's row
+// starts at rp[j], B's dB bytes further.
+template <typename T, bool DUAL>
+struct GLULoader {
+  static constexpr bool kDirect = false;
+  static constexpr int RPL = 1024 / ROWB;  // rows per 1 KB load
+  static constexpr int NPL = 32 / RPL;     // loads per thread per k-tile
+  const char* rp[NPL];
+  int64_t dB;
+  int c0, klen;
+  uint4 ra[NPL], rb[NPL];
+
+  __device__ __forceinline__ void setup(const T* A, const T* B, const int32_t* list, int rbeg,
+                                        int rend, int h) {
+    KLoaderD<T> tmp;
+    tmp.init_chunks();
+    c0 = tmp.c0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int li = rbeg + KLoaderD<T>::row_of(j);
+      rp[j] = li < rend ? reinterpret_cast<const char*>(A + (int64_t)list[li] * h) : nullptr;
+    }
+    dB = DUAL ? reinterpret_cast<const char*>(B) - reinterpret_cast<const char*>(A) : 0;
+    klen = h;
+  }
+  // load j of a KLoaderD fetches logical chunk c0 ^ j
+  __device__ __forceinline__ int chunk_of(int j) const { return c0 ^ j; }
+  __device__ __forceinline__ void fetch(int kt) {
+    constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int k = kt * KT + chunk_of(j) * VEC;
+      const bool ok = rp[j] != nullptr && k < klen;
+      const char* g = ok ? rp[j] + (int64_t)k * ES : nullptr;
+      ra[j] = ok ? *reinterpret_cast<const uint4*>(g) : make_uint4(0, 0, 0, 0);
+      rb[j] = (ok && DUAL) ? *reinterpret_cast<const uint4*>(g + dB) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      *reinterpret_cast<uint4*>(lds + (w * 32 + RPL * j) * ROWB + lane * 16) =
+          glu16<T>(ra[j], rb[j], DUAL, 1.0f);
+  }
+};
+
+// gate * G of the dW2 product, bf16: the TLoaderD layout ([k = route][h
+// position], 512 bytes per k-row) filled from registers; route p = rbase + k
+// (an expert's routes are contiguous), gate gate_p[p].
+template <bool DUAL>
+struct TGLULoader {
+  static constexpr bool kDirect = false;
+  const char* col[4];     // A's column of load j (route 0); absent: nullptr
+  int64_t ld, dB;
+  int64_t rbase;
+  int klen;
+  const float* gate_p;
+  uint4 ra[4], rb[4];
+  float g[4];
+
+  __device__ __forceinline__ void setup(const bf16_t* A, const bf16_t* B, int first_pos,
+                                        int limit, int h, int64_t rbase_, int klen_,
+                                        const float* gate_p_) {
+    ld = (int64_t)h * 2;
+    dB = DUAL ? reinterpret_cast<const char*>(B) - reinterpret_cast<const char*>(A) : 0;
+    rbase = rbase_;
+    klen = klen_;
+    gate_p = gate_p_;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = first_pos + TLoaderD::lpos(j);
+      col[j] = p < limit ? reinterpret_cast<const char*>(A) + (int64_t)p * 2 : nullptr;
+    }
+  }
+  __device__ __forceinline__ void fetch(int kt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = kt * 64 + TLoaderD::krow(j);
+      const bool ok = col[j] != nullptr && k < klen;
+      const char* a = ok ? col[j] + (rbase + k) * ld : nullptr;
+      ra[j] = ok ? *reinterpret_cast<const uint4*>(a) : make_uint4(0, 0, 0, 0);
+      rb[j] = (ok && DUAL) ? *reinterpret_cast<const uint4*>(a + dB) : make_uint4(0, 0, 0, 0);
+      g[j] = k < klen ? gate_p[rbase + k] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(lds + (w * 8 + 2 * j) * 512 + lane * 16) =
+          glu16<bf16_t>(ra[j], rb[j], DUAL, g[j]);
+  }
+};
+
+// gate * G of the dW2 product, float32: the MNLoader layout (positions
+// contiguous in memory, transposed in registers on the way into LDS).
+template <bool DUAL>
+struct MNGLULoader {
+  static constexpr bool kDirect = false;
+  MNLoader<float> a, b;
+  const float* gate_p;
+  int64_t rbase;
+  int klen;
+  float g[4];
+
+  __device__ __forceinline__ void setup(const float* A, const float* B, int first_pos, int limit,
+                                        int h, int64_t rbase_, int klen_, const float* gate_p_) {
+    a.setup(reinterpret_cast<const char*>(A), first_pos, limit, (int64_t)h * 4, nullptr, rbase_,
+            klen_);
+    if (DUAL)
+      b.setup(reinterpret_cast<const char*>(B), first_pos, limit, (int64_t)h * 4, nullptr, rbase_,
+              klen_);
+    gate_p = gate_p_;
+    rbase = rbase_;
+    klen = klen_;
+  }
+  __device__ __forceinline__ void fetch(int kt) {
+    a.fetch(kt);
+    if (DUAL) b.fetch(kt);
+    const int k0 = kt * Traits<float>::KT + MNLoader<float>::krow0();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g[i] = k0 + i < klen ? gate_p[rbase + k0 + i] : 0.f;
+  }
+  __device__ __forceinline__ void store(char* lds) {
+    // a.reg[i] holds 4 positions of k-row k0 + i: apply gate * SiLU(A) [* B]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a.reg[i] = glu16<float>(a.reg[i], DUAL ? b.reg[i] : make_uint4(0, 0, 0, 0), DUAL, g[i]);
+    a.store(lds);
+  }
+};
+
 // ------------------------------------------------------------------ kernels
 
 struct RouteArgs {            // row tiles over routes or slot-pass lists
@@ -886,9 +1061,9 @@ __device__ __forceinline__ void lds8(const float* p, float v[8]) {
 }
 
 // F1: [A | B] = X W1 [| X W3] with X gathered by expert_token_indices;
-// epilogue writes A, B (checkpoint) and G = SiLU(A) [* B].
+// epilogue writes A, B (checkpoint) and, with KEEPG, G = SiLU(A) [* B].
 // W1T, W3T: [E, h, d] (transposed weights).
-template <typename T, bool DUAL>
+template <typename T, bool DUAL, bool KEEPG>
 __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __restrict__ x,
                                                        const T* __restrict__ W1T,
                                                        const T* __restrict__ W3T,
@@ -954,7 +1129,7 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
           const float a = acc.c[mt][0][i], b = acc.c[mt][1][i];
           Elem<T>::store(byte_off(At, o), a);
           Elem<T>::store(byte_off(Bt, o), b);
-          Elem<T>::store(byte_off(Gt, o), silu_of<T>(a) * b);
+          if (KEEPG) Elem<T>::store(byte_off(Gt, o), silu_of<T>(a) * b);
         }
       }
     } else {
@@ -972,7 +1147,7 @@ __global__ __launch_bounds__(NT, 1) void f1_gather_glu(RouteArgs ra, const T* __
             const uint32_t o = vo + (uint32_t)(ru * h) * (uint32_t)sizeof(T);
             const float a = acc.c[mt][nt][i];
             Elem<T>::store(byte_off(At, o), a);
-            Elem<T>::store(byte_off(Gt, o), silu_of<T>(a));
+            if (KEEPG) Elem<T>::store(byte_off(Gt, o), silu_of<T>(a));
           }
         }
       }
@@ -1102,9 +1277,12 @@ __device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, con
 }
 
 // F2 (slot pass k): O = G W2_e for the pass's rows, y[t] (+)= gate * O.
-// W2T: [E, d, h] (transposed weights).
-template <typename T>
+// W2T: [E, d, h] (transposed weights).  GM = 0: G read from Gb; GM = 1 / 2:
+// G = SiLU(A) / SiLU(A) * B formed from the checkpoint at operand load.
+template <typename T, int GM>
 __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* __restrict__ Gb,
+                                                         const T* __restrict__ Ab,
+                                                         const T* __restrict__ Bb,
                                                          const T* __restrict__ W2T,
                                                          const int32_t* __restrict__ list,
                                                          const int32_t* __restrict__ eti,
@@ -1133,16 +1311,22 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
     s_g[threadIdx.x] = g;
   }
 
-  KLoaderD<T> la;
-  kloaderd_rows<T>(la, Gb, list, nullptr, rb, re, h, ra.zero);
-  la.delta = 0;
-  la.ksplit = la.klen = h;
   KLoaderD<T> lb;
   kloaderd_rows<T>(lb, W2T + (int64_t)e * d * h, nullptr, nullptr, n0, d, h, ra.zero);
   lb.delta = 0;
   lb.ksplit = lb.klen = h;
   Acc acc;
-  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
+  if constexpr (GM == 0) {
+    KLoaderD<T> la;
+    kloaderd_rows<T>(la, Gb, list, nullptr, rb, re, h, ra.zero);
+    la.delta = 0;
+    la.ksplit = la.klen = h;
+    gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
+  } else {
+    GLULoader<T, GM == 2> la;
+    la.setup(Ab, Bb, list, rb, re, h);
+    gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
+  }
   __syncthreads();
   combine_dispatch<T>(acc, smem, s_t, s_g, re - rb, n0, d, mode, y, yacc);
 }
@@ -1156,7 +1340,7 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
 // butterfly, so the value does not depend on timing.  FULL: all rows present
 // and all columns inside h, so no store sits under a branch (see
 // combine_epilogue for why that matters to the waits on the loads).
-template <typename T, bool DUAL, bool ROUTER, bool FULL>
+template <typename T, bool DUAL, bool ROUTER, bool FULL, bool KEEPG>
 __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const float* s_g, int rb,
                                             int re, int n0, int h, int nN, int ntile,
                                             T* __restrict__ A, T* __restrict__ B,
@@ -1222,7 +1406,7 @@ __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const fl
         }
         store8(A + o, da);
         if (DUAL) store8(B + o, db);
-        store8(Gs + o, gs);
+        if (KEEPG) store8(Gs + o, gs);
       }
       if (ROUTER) {
 #pragma unroll
@@ -1240,7 +1424,7 @@ __device__ __forceinline__ void b1_epilogue(const Acc& acc, char* smem, const fl
 // also leaves, for every route row p, the tile's share of the router
 // gradient's <dy[t] W2_e^T, G[p]> (= <dy[t], O[p]>, O the route's un-gated
 // output) in dgp[p * nN + ntile].
-template <typename T, bool DUAL, bool ROUTER>
+template <typename T, bool DUAL, bool ROUTER, bool KEEPG>
 __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __restrict__ dy,
                                                       const T* __restrict__ W2,
                                                       const int32_t* __restrict__ eti,
@@ -1277,9 +1461,11 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
   __syncthreads();
 
   if (__builtin_amdgcn_readfirstlane((re - rb == TBM && n0 + 256 <= h) ? 1 : 0))
-    b1_epilogue<T, DUAL, ROUTER, true>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+    b1_epilogue<T, DUAL, ROUTER, true, KEEPG>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs,
+                                              dgp);
   else
-    b1_epilogue<T, DUAL, ROUTER, false>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B, Gs, dgp);
+    b1_epilogue<T, DUAL, ROUTER, false, KEEPG>(acc, smem, s_g, rb, re, n0, h, ra.nN, ntile, A, B,
+                                               Gs, dgp);
 }
 
 // Router gradient, one workgroup per TB tokens (TB * E <= 16384: 64 tokens
@@ -1360,8 +1546,14 @@ __device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& m
 }
 
 // B0: dW2_e = Gs_e^T dy_e (reduction over the expert's routes, ascending).
-template <typename T>
+// GM = 0: Gs = gate * G read from the buffer the dG kernel wrote; GM = 1 / 2:
+// formed at operand load from the checkpoint A [, B] and the route gates
+// (this kernel then runs before the dG kernel replaces A and B).
+template <typename T, int GM>
 __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restrict__ Gs,
+                                                const T* __restrict__ Ab,
+                                                const T* __restrict__ Bb,
+                                                const float* __restrict__ gate_p,
                                                 const T* __restrict__ dy,
                                                 const int32_t* __restrict__ eti,
                                                 const int32_t* __restrict__ offsets, int d, int h,
@@ -1377,18 +1569,33 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
 
   Acc acc;
   if constexpr (std::is_same<T, bf16_t>::value) {
-    TLoaderD la, lb;
-    la.setup<false>(reinterpret_cast<const char*>(Gs), nullptr, m0, h, (int64_t)h * ES, nullptr,
-                    o0, n_e, wa.zero);
+    TLoaderD lb;
     lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
                     0, n_e, wa.zero);
-    gemm_mainloop<T, TLoaderD, TLoaderD, true, false, true>(la, lb, (n_e + KT - 1) / KT, smem, acc,
-                                                            live);
+    if constexpr (GM == 0) {
+      TLoaderD la;
+      la.setup<false>(reinterpret_cast<const char*>(Gs), nullptr, m0, h, (int64_t)h * ES, nullptr,
+                      o0, n_e, wa.zero);
+      gemm_mainloop<T, TLoaderD, TLoaderD, true, false, true>(la, lb, (n_e + KT - 1) / KT, smem,
+                                                              acc, live);
+    } else {
+      TGLULoader<GM == 2> la;
+      la.setup(Ab, Bb, m0, h, h, o0, n_e, gate_p);
+      gemm_mainloop<T, TGLULoader<GM == 2>, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem,
+                                                             acc);
+    }
   } else {
-    MNLoader<T> la, lb;
-    la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
+    MNLoader<T> lb;
     lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    if constexpr (GM == 0) {
+      MNLoader<T> la;
+      la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
+      gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    } else {
+      MNGLULoader<GM == 2> la;
+      la.setup(Ab, Bb, m0, h, h, o0, n_e, gate_p);
+      gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
+    }
   }
 
   T* out = dW2 + (int64_t)e * h * d;
@@ -1527,7 +1734,8 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   const bool need_acc = dm.dtype == 1 && dm.K > 1;
   const size_t wbytes = (size_t)dm.E * dm.d * dm.h * es;
   size_t o = 0;
-  p.off_g = o;      o = align_up(o + (size_t)p.R * dm.h * es, 256);
+  // G (forward) or gate * G (backward), unless the second GEMMs form it from A, B
+  p.off_g = o;      o = align_up(o + (dm.recompute_g ? 0 : (size_t)p.R * dm.h * es), 256);
   p.off_acc = o;    o = align_up(o + (need_acc ? (size_t)dm.L * dm.d * 4 : 0), 256);
   p.off_slot = o;   o = align_up(o + (size_t)p.R + 16, 256);
   p.off_list = o;   o = align_up(o + (size_t)p.R * 4, 256);
@@ -1623,23 +1831,31 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
   Lists ls = build_lists(pl, dm, offsets, tim, gates, nullptr, ws, s);
   T* G = reinterpret_cast<T*>(ws + pl.off_g);
   float* acc = f32 ? reinterpret_cast<float*>(y) : reinterpret_cast<float*>(ws + pl.off_acc);
+  const bool keepg = !dm.recompute_g;
   {
     LaunchTimer lt("ffn_f1_gather_glu", s);
     RouteArgs ra{ls.tiles_route, pl.route_tiles, (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero, 4};
     const unsigned grid = (unsigned)route_grid(ra);
-    if (dual)
-      hipLaunchKernelGGL((f1_gather_glu<T, true>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
-                         eti, dm.d, dm.h, A, B, G);
-    else
-      hipLaunchKernelGGL((f1_gather_glu<T, false>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T,
-                         eti, dm.d, dm.h, A, B, G);
+#define MOE_F1(DU, KG)                                                                          \
+  hipLaunchKernelGGL((f1_gather_glu<T, DU, KG>), dim3(grid), dim3(NT), 0, s, ra, x, W1T, W3T, eti, \
+                     dm.d, dm.h, A, B, G)
+    if (dual) {
+      if (keepg) MOE_F1(true, true); else MOE_F1(true, false);
+    } else {
+      if (keepg) MOE_F1(false, true); else MOE_F1(false, false);
+    }
+#undef MOE_F1
   }
+  const int gm = keepg ? 0 : (dual ? 2 : 1);
   for (int k = 0; k < dm.K; ++k) {
     LaunchTimer lt("ffn_f2_down_combine", s);
     RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero, 1};
     const unsigned grid = (unsigned)route_grid(ra);
-    hipLaunchKernelGGL((f2_down_combine<T>), dim3(grid), dim3(NT), 0, s, ra, G, W2T, ls.list, eti,
-                       gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc);
+#define MOE_F2(GMV)                                                                             \
+  hipLaunchKernelGGL((f2_down_combine<T, GMV>), dim3(grid), dim3(NT), 0, s, ra, G, A, B, W2T,     \
+                     ls.list, eti, gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc)
+    if (gm == 0) MOE_F2(0); else if (gm == 1) MOE_F2(1); else MOE_F2(2);
+#undef MOE_F2
   }
 }
 
@@ -1656,20 +1872,38 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   float* acc = f32 ? reinterpret_cast<float*>(dx) : reinterpret_cast<float*>(ws + pl.off_acc);
   float* dgp = dlogits != nullptr ? reinterpret_cast<float*>(ws + pl.off_dgp) : nullptr;
   const int nNh = (int)cdiv(dm.h, 256);
+  const bool keepg = !dm.recompute_g;
+  const int gm = keepg ? 0 : (dual ? 2 : 1);
+  // dW2 needs gate * G: from the dG kernel's buffer (after it), or formed
+  // from A, B (before the dG kernel writes dA, dB over them)
+  auto dw2 = [&]() {
+    LaunchTimer lt("ffn_b0_dw2", s);
+    WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256), (const char*)ls.zero};
+    const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
+#define MOE_B0(GMV)                                                                             \
+  hipLaunchKernelGGL((b0_dw2<T, GMV>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, A, B,    \
+                     gate_p, dy, eti, offsets, dm.d, dm.h, dW2)
+    if (gm == 0) MOE_B0(0); else if (gm == 1) MOE_B0(1); else MOE_B0(2);
+#undef MOE_B0
+  };
+  if (!keepg) dw2();
   {
     LaunchTimer lt("ffn_b1_dgrad_glu", s);
     RouteArgs ra{ls.tiles_route, pl.route_tiles, nNh, (const char*)ls.zero, 1};
     const unsigned grid = (unsigned)route_grid(ra);
-#define MOE_B1(DU, RO)                                                                          \
-  hipLaunchKernelGGL((b1_dgrad_glu<T, DU, RO>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti, gate_p, \
-                     dm.d, dm.h, A, B, Gs, dgp)
+#define MOE_B1(DU, RO, KG)                                                                      \
+  hipLaunchKernelGGL((b1_dgrad_glu<T, DU, RO, KG>), dim3(grid), dim3(NT), 0, s, ra, dy, W2, eti,  \
+                     gate_p, dm.d, dm.h, A, B, Gs, dgp)
+#define MOE_B1K(DU, RO) \
+  if (keepg) MOE_B1(DU, RO, true); else MOE_B1(DU, RO, false)
     if (dual) {
-      if (dgp != nullptr) MOE_B1(true, true);
-      else MOE_B1(true, false);
+      if (dgp != nullptr) MOE_B1K(true, true);
+      else MOE_B1K(true, false);
     } else {
-      if (dgp != nullptr) MOE_B1(false, true);
-      else MOE_B1(false, false);
+      if (dgp != nullptr) MOE_B1K(false, true);
+      else MOE_B1K(false, false);
     }
+#undef MOE_B1K
 #undef MOE_B1
   }
   if (dlogits != nullptr) {
@@ -1678,13 +1912,7 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
     hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, TB)), dim3(256), 0, s, tei, tim,
                        gates, dgp, nNh, dm.L, dm.E, dm.K, TB, dlogits);
   }
-  {
-    LaunchTimer lt("ffn_b0_dw2", s);
-    WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256), (const char*)ls.zero};
-    const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
-    hipLaunchKernelGGL((b0_dw2<T>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, dy, eti,
-                       offsets, dm.d, dm.h, dW2);
-  }
+  if (keepg) dw2();
   {
     LaunchTimer lt("ffn_b2_dw13", s);
     WeightArgs wa{dm.E, (int)cdiv(dm.d, 256), (int)cdiv(dm.h, dual ? 128 : 256), (const char*)ls.zero};

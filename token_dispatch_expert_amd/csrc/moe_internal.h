@@ -41,6 +41,7 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
 struct FfnDims {
   int64_t L;
   int d, h, E, K, dtype, act;
+  bool recompute_g;  // no G buffer: the second GEMMs form G from A, B
 };
 
 struct FfnPlan {

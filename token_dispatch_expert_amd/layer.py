@@ -16,9 +16,11 @@ from .workloads import MoEConfig, SWIGLU, F32
 
 class MoELayerBuffers:
     """router_grad=True also allocates dlogits [L, E] float32 and asks the
-    backward for the router-logit gradient."""
+    backward for the router-logit gradient.  recompute_g=True sets
+    MOE_FLAG_RECOMPUTE_G: no [L*K, h] G buffer in the workspace."""
 
-    def __init__(self, cfg: MoEConfig, device="cuda", router_grad: bool = False):
+    def __init__(self, cfg: MoEConfig, device="cuda", router_grad: bool = False,
+                 recompute_g: bool = False):
         self.cfg = cfg
         self.device = torch.device(device)
         L, d, h, E, K = cfg.L, cfg.d, cfg.h, cfg.E, cfg.K
@@ -27,7 +29,8 @@ class MoELayerBuffers:
         dev = self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.shape = B.make_shape(L, d, h, E, K, B.MOE_F32 if cfg.dtype == F32 else B.MOE_BF16,
-                                  B.MOE_SWIGLU if cfg.act == SWIGLU else B.MOE_SILU)
+                                  B.MOE_SWIGLU if cfg.act == SWIGLU else B.MOE_SILU,
+                                  B.MOE_FLAG_RECOMPUTE_G if recompute_g else 0)
         self.eti = torch.empty(R, **i32)
         self.offsets = torch.empty(E + 1, **i32)
         self.tei = torch.empty(L, K, **i32)
