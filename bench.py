@@ -101,9 +101,13 @@ def dispatch_bytes_byte_map(cfg):
     return 4 * L * E + 3 * L * E + 16 * L * K + 4 * (E + 1)
 
 
-def source_hash():
+def source_hash(timer):
+    """Hash of the sources a timer's kernels are built from (their .hip file
+    and the shared headers), so that counters stay valid for kernels that did
+    not change."""
+    src = "ffn.hip" if timer.startswith("ffn_") else "dispatch.hip"
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "token_dispatch_expert_amd", "csrc"))):
+    for f in (src, "moe_device.h", "moe_internal.h"):
         with open(os.path.join(ROOT, "token_dispatch_expert_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -154,7 +158,7 @@ def record_traffic(dirs, workload):
     ent = {}
     for timer, sym in ROCPROF_NAMES.items():
         if sym in fetch and sym in write:
-            ent[timer] = {"source_hash": source_hash(),
+            ent[timer] = {"source_hash": source_hash(timer),
                           "fetch_bytes_per_launch": fetch[sym] * fscale,
                           "write_bytes_per_launch": write[sym] * wscale,
                           "bytes_per_launch": fetch[sym] * fscale + write[sym] * wscale}
@@ -175,7 +179,7 @@ def measured_traffic(kernel, workload):
     with open(p) as f:
         rec = json.load(f)
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_hash") != source_hash():
+    if not ent or ent.get("source_hash") != source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 

@@ -400,7 +400,11 @@ __global__ __launch_bounds__(64) void k1_route_mask(const float* __restrict__ lo
   constexpr int PART = 64 * 4 * EB + (VEC ? 0 : 1024);  // LDS bytes
   __shared__ __attribute__((aligned(16))) char stage[PART];
   const int lane = threadIdx.x;
-  const int64_t part = blockIdx.x;
+  int64_t part;
+  {  // contiguous runs of parts per XCD: neighbouring parts' count words meet in one L2
+    const int64_t nb = gridDim.x, b = blockIdx.x, q = nb >> 3, r = nb & 7, x = b & 7;
+    part = x * q + (x < r ? x : r) + (b >> 3);
+  }
   const int rowb = 4 * E;
   RouteSrc src;
   {
