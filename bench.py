@@ -400,7 +400,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
+        print("bench.py measures one GPU: the layer runs on a single MI355X here "
               "and has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
