@@ -7,6 +7,10 @@ silently take away, each of which has cost 10-30 % when it went missing:
 * between the direct-to-LDS copies of the next k-tile and the fragment reads
   of the current one there is no wait on the vector-memory counter (such a
   wait serialises copies and MFMAs);
+* no such wait sits between two copies either: the compiler does not count
+  the copies (inline assembly), so a wait it places for a load of its own
+  (a spill reload, an index) also waits for every copy already issued, and
+  the copies of a k-tile then go out one at a time;
 * M0, which the copies set, is written by nothing else.
 """
 
@@ -102,6 +106,26 @@ def test_no_copy_wait_before_fragment_reads(asm):
                 assert not waited, f"{name}: vmcnt wait between the copies and {line.split()[0]}"
                 checked += 1
     assert checked >= len(GEMMS)
+
+
+def test_no_wait_between_copies(asm):
+    """Inside one basic block, no vmcnt wait separates two direct-to-LDS
+    copies in any GEMM kernel (bf16 and float32, every mode)."""
+    copies = 0
+    for name, body in _kernels(asm).items():
+        if not any(g in name for g in GEMMS):
+            continue
+        after_copy = waited = False
+        for line in body:
+            if line.startswith("global_load_lds"):
+                assert not (after_copy and waited), f"{name}: vmcnt wait between two copies"
+                after_copy, waited = True, False
+                copies += 1
+            elif line.startswith((".LBB", "s_branch", "s_cbranch", "s_barrier")):
+                after_copy = waited = False
+            elif after_copy and line.startswith("s_waitcnt") and "vmcnt" in line:
+                waited = True
+    assert copies >= 8 * len(GEMMS)
 
 
 def test_m0_written_only_by_the_copies(asm):
