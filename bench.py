@@ -113,15 +113,16 @@ def source_hash(timer):
     return h.hexdigest()[:16]
 
 
-ROCPROF_NAMES = {   # library timer name -> kernel symbol base name in rocprofv3 output
-    "ffn_f1_gather_glu": "f1_gather_glu",
-    "ffn_f2_down_combine": "f2_down_combine",
-    "ffn_b1_dgrad_glu": "b1_dgrad_glu",
-    "ffn_b0_dw2": "b0_dw2",
-    "ffn_b2_dw13": "b2_dw13",
-    "ffn_b3_dx": "b3_dx",
-    "dispatch_route_map": "k1_route_mask",     # E <= 64, K <= 8 (k1_route_wide_mask beyond, k1_route_map* for K > 8)
-    "dispatch_scatter": "k3_scatter_mask",
+ROCPROF_NAMES = {   # library timer name -> kernel symbol base names in rocprofv3 output (first found)
+    "ffn_f1_gather_glu": ("f1_gather_glu",),
+    "ffn_f2_down_combine": ("f2_down_combine",),
+    "ffn_b1_dgrad_glu": ("b1_dgrad_glu",),
+    "ffn_b0_dw2": ("b0_dw2",),
+    "ffn_b2_dw13": ("b2_dw13",),
+    "ffn_b3_dx": ("b3_dx",),
+    # E == 64 with aligned rows and L >= 64, else E <= 64 (k1_route_wide_mask beyond 64)
+    "dispatch_route_map": ("k1_route_mask64", "k1_route_mask"),
+    "dispatch_scatter": ("k3_scatter_mask",),
 }
 
 
@@ -156,8 +157,9 @@ def record_traffic(dirs, workload):
     p = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(p)) if os.path.exists(p) else {}
     ent = {}
-    for timer, sym in ROCPROF_NAMES.items():
-        if sym in fetch and sym in write:
+    for timer, syms in ROCPROF_NAMES.items():
+        sym = next((n for n in syms if n in fetch and n in write), None)
+        if sym is not None:
             ent[timer] = {"source_hash": source_hash(timer),
                           "fetch_bytes_per_launch": fetch[sym] * fscale,
                           "write_bytes_per_launch": write[sym] * wscale,

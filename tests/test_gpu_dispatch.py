@@ -59,6 +59,9 @@ EDGE = [
     (2500, 28, 7, "normal"),        # streaming router, 7 chunks per row
     (3000, 40, 8, "normal"),        # 64-bit expert mask with E < 64
     (3001, 64, 8, "ties"),          # largest streaming E and K
+    (64, 64, 6, "normal"),          # one whole part on the 64-expert register-load router
+    (65, 64, 2, "normal"),          # its last part read from row 1, 63 rows back
+    (63, 64, 4, "normal"),          # fewer than 64 tokens: the direct-to-LDS router
     (1500, 128, 8, "ties"),         # lane-pair router (E <= 128), ties at the K-th value
     (2000, 200, 5, "normal"),       # lane-quad router, last lane partly empty
     (1200, 130, 3, "normal"),       # lane-quad router, E not a multiple of 4

@@ -431,6 +431,53 @@ __global__ __launch_bounds__(64) void k1_route_mask(const float* __restrict__ lo
   }
 }
 
+// Step 1, streaming form for exactly 64 experts with 16-byte aligned rows
+// and L >= 64: as k1_route_mask, but the part's 16 KB of logits come in
+// through registers (sixteen coalesced 16-byte loads per lane, all in flight
+// together) and the wavefront writes them into LDS itself, which moves
+// 256-byte rows faster than the direct-to-LDS copies.  The last part reads
+// rows [L - 64, L) instead of running past the end, so every load is in
+// range; token t then sits in stage row t - first_row.
+template <int KM>
+__global__ __launch_bounds__(64) void k1_route_mask64(const float* __restrict__ logits, int64_t L,
+                                                      int E, int K, int64_t NP,
+                                                      int32_t* __restrict__ tei,
+                                                      float* __restrict__ gates,
+                                                      uint64_t* __restrict__ tmask,
+                                                      uint64_t* __restrict__ tcol,
+                                                      int32_t* __restrict__ partcnt) {
+  constexpr int NQ = 16;  // 16-byte loads per lane (E == 64)
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __shared__ v4f stage[64 * NQ];
+  const int lane = threadIdx.x;
+  int64_t part;
+  {  // contiguous runs of parts per XCD: neighbouring parts' count words meet in one L2
+    const int64_t nb = gridDim.x, b = blockIdx.x, q = nb >> 3, r = nb & 7, x = b & 7;
+    part = x * q + (x < r ? x : r) + (b >> 3);
+  }
+  const int64_t first_row = min(part * 64, L - 64);
+  const v4f* pb = reinterpret_cast<const v4f*>(logits) + first_row * NQ;  // uniform
+  v4f v[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) v[c] = __builtin_nontemporal_load(pb + c * 64 + lane);
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) stage[c * 64 + lane] = v[c];
+  __builtin_amdgcn_wave_barrier();
+  const int64_t t = part * 64 + lane;
+  // rows past L (last part only) route a valid row and store nothing
+  const int srow = (int)min<int64_t>(t - first_row, 63);
+  // E (64) comes in as an argument: the selection then loops over the row's
+  // chunks instead of unrolling all of them into registers
+  const float* row = reinterpret_cast<const float*>(stage) + srow * E;
+  const uint64_t m = route_row<64, KM, true>(row, E, K, lane, t < L, t, tei, gates);
+  if (t < L) tmask[t] = m;
+  uint32_t col_lo = 0, col_hi = 0;
+  BallotColumns<0, 64>::run(m, col_lo, col_hi);
+  const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+  tcol[part * E + lane] = mycol;
+  partcnt[(int64_t)lane * NP + part] = __popcll(mycol);
+}
+
 // Step 3 for the streaming form: one workgroup per 256-token tile, one
 // wavefront per 64-token part.  A token's position in expert e's segment is
 // the segment start, plus the tokens of e in earlier tiles (scanned counts),
@@ -1110,8 +1157,12 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
       uint64_t* tmask = reinterpret_cast<uint64_t*>(ws + pl.off_map);
       uint64_t* tcol = reinterpret_cast<uint64_t*>(ws + pl.off_col);
 #define K1M(EBV, KV, VV)                                                                        \
-  hipLaunchKernelGGL((k1_route_mask<EBV, KV, VV>), dim3(pl.NP), dim3(64), 0, s, logits, L, E, K, \
-                     pl.NP, tei, gates, tmask, tcol, cnt)
+  if (VV && EBV == 64 && E == 64 && L >= 64)                                                    \
+    hipLaunchKernelGGL((k1_route_mask64<KV>), dim3(pl.NP), dim3(64), 0, s, logits, L, E, K,       \
+                       pl.NP, tei, gates, tmask, tcol, cnt);                                    \
+  else                                                                                          \
+    hipLaunchKernelGGL((k1_route_mask<EBV, KV, VV>), dim3(pl.NP), dim3(64), 0, s, logits, L, E,   \
+                       K, pl.NP, tei, gates, tmask, tcol, cnt)
 #define K1M_K(EBV)                                                                              \
   if (!rows_ok) {                                                                               \
     K1M(EBV, 8, false);                                                                         \
