@@ -487,7 +487,7 @@ __global__ __launch_bounds__(64) void k1_route_mask64(const float* __restrict__ 
 // that segment: the tile collects its entries in LDS ordered by expert and
 // writes them out run by run.  Tiles are spread over the XCDs in contiguous
 // ranges so that neighbouring runs meet in one L2.
-template <int RW>
+template <int RW, int KMAX>
 __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restrict__ tmask,
                                                        const uint64_t* __restrict__ tcol,
                                                        int64_t L, int E, int K, int NU,
@@ -496,7 +496,9 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
                                                        int32_t* __restrict__ eti,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ tim) {
-  constexpr int MAXE = 256 * 8;  // entries of one tile (K <= 8)
+  // entries of one tile (K <= KMAX): the staging arrays are sized for the
+  // layer's K bucket, so that smaller K leaves room for more workgroups per CU
+  constexpr int MAXE = 256 * KMAX;
   __shared__ int s_off[257];
   __shared__ int scratch[4];
   __shared__ uint64_t s_col[4][64];
@@ -1247,9 +1249,15 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
 #define K3W(WV)                                                                                 \
   hipLaunchKernelGGL(k3_scatter_wide<WV>, dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K, pl.C, \
                      base, total, eti, offsets, tim)
-    if (pl.stream && pl.W == 1)
-      hipLaunchKernelGGL(k3_scatter_mask<4>, dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K,
-                         pl.C, base, total, eti, offsets, tim);
+#define K3M(KX)                                                                                 \
+  hipLaunchKernelGGL((k3_scatter_mask<4, KX>), dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K,  \
+                     pl.C, base, total, eti, offsets, tim)
+    if (pl.stream && pl.W == 1) {
+      if (K <= 2) K3M(2);
+      else if (K <= 4) K3M(4);
+      else if (K <= 6) K3M(6);
+      else K3M(8);
+    }
     else if (pl.stream && pl.W == 2)
       K3W(2);
     else if (pl.stream && pl.W == 4)
@@ -1259,6 +1267,7 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
     else if (pl.stream)
       K3W(16);
 #undef K3W
+#undef K3M
     else
       hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
                          base, total, eti, offsets, tim);
