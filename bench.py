@@ -226,7 +226,7 @@ def _emit(d):
 
 def study_memory(cfg, seed, dev, steps=3):
     """Device memory and step time of one layer step, with G kept between
-    the two GEMMs of each pass (default) and with G formed at operand load
+    the two GEMMs of each pass (default) and with G formed in [L, h] pieces
     (MOE_FLAG_RECOMPUTE_G): what the method keeps between forward and
     backward (A, B), the transient buffers, the measured peak (torch's
     allocator holds every buffer), and, for scale, the two (L*K, d) buffers
@@ -254,9 +254,9 @@ def study_memory(cfg, seed, dev, steps=3):
         B.profile_enable(False)
         st = B.profile_read()
         _emit({"study": "memory", "workload": cfg.name,
-               "mode": "G formed at operand load" if recompute else "G kept",
+               "mode": "G formed in L-row pieces" if recompute else "G kept",
                "checkpoint_bytes": cfg.R * cfg.h * (2 if cfg.act == W.SWIGLU else 1) * es,
-               "transient_G_bytes": 0 if recompute else cfg.R * cfg.h * es,
+               "transient_G_bytes": (cfg.L if recompute else cfg.R) * cfg.h * es,
                "workspace_bytes": int(buf.ws.numel()),
                "inputs_bytes": int(m_inputs),
                "layer_buffers_bytes": int(m_buffers - m_inputs),
@@ -373,7 +373,7 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute-g", action="store_true",
-                    help="MOE_FLAG_RECOMPUTE_G: no G buffer; the second GEMMs form G from A, B")
+                    help="MOE_FLAG_RECOMPUTE_G: G formed from A, B in [L, h] pieces, no [L*K, h] buffer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scale reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -471,7 +471,7 @@ def main():
         "config": {"workload": cfg.name, "L": cfg.L, "d": cfg.d, "h": cfg.h, "E": cfg.E,
                    "K": cfg.K, "act": "swiglu" if cfg.act == W.SWIGLU else "silu",
                    "seed": seed, "parallelism": "none (1 GPU)",
-                   "g_buffer": "none (G formed at operand load)" if args.recompute_g else "kept"},
+                   "g_buffer": "[L, h] pieces" if args.recompute_g else "kept"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "flops_per_launch": kflops[dom],

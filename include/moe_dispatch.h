@@ -74,15 +74,16 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_SILU = 0, MOE_SWIGLU = 1 };
 
 /* Flags of moe_shape.flags (0 = none).
- *   MOE_FLAG_RECOMPUTE_G: keep no copy of G = SiLU(A) [* B] between the
- *     two GEMMs of either pass.  The forward stores only A and B; its
- *     second GEMM forms G from A and B as it loads its operand, and the
- *     backward forms gate * G the same way for dW2 (before dA, dB replace
- *     A, B).  The workspace then holds no [L*K, h] buffer (half the
- *     checkpoint's size for SwiGLU, all of it for SiLU) at the price of
- *     reading A and B instead of G.  Results agree with the default within
- *     the bf16 rounding of G (G is formed from the stored A, B instead of
- *     their float32 accumulators). */
+ *   MOE_FLAG_RECOMPUTE_G: keep no [L*K, h] copy of G = SiLU(A) [* B]
+ *     between the two GEMMs of either pass.  The forward stores only A and
+ *     B; before each of its K slot passes it forms that pass's L rows of G
+ *     from A and B into an [L, h] piece of the workspace, and the backward
+ *     forms gate * G the same way for dW2, one group of experts (at most L
+ *     routes) at a time, before dA, dB replace A, B.  The workspace then
+ *     holds one [L, h] piece instead of the [L*K, h] buffer, at the price
+ *     of reading A and B once more per piece.  Results agree with the
+ *     default within the bf16 rounding of G (G is formed from the stored
+ *     A, B instead of their float32 accumulators). */
 enum { MOE_FLAG_RECOMPUTE_G = 1 };
 
 typedef struct moe_shape {

@@ -158,7 +158,7 @@ def run_sampled_parity(cfg, seed, device, n_tokens=4096, recompute_g=False):
     heaviest, the lightest non-empty and one random other expert (whole
     matrices where the oracle runs them in seconds, else a column subset
     covering whole tiles), and exact zeros for every empty expert."""
-    say(f"  sampled parity {cfg.name} seed {seed}" + (" (G formed at operand load)" if recompute_g else ""))
+    say(f"  sampled parity {cfg.name} seed {seed}" + (" (G formed in [L, h] pieces)" if recompute_g else ""))
     inp = W.make_inputs(cfg, seed, device)
     buf = MoELayerBuffers(cfg, device, router_grad=True, recompute_g=recompute_g)
     logits = inp["logits"].cpu().numpy()

@@ -272,15 +272,16 @@ def test_expert_counts_up_to_1024_accepted(lib):
 
 
 def test_recompute_g_drops_the_g_buffer(lib):
-    """MOE_FLAG_RECOMPUTE_G removes exactly one [L*K, h] buffer from the
-    forward and the backward workspace; unknown flag bits are rejected."""
-    for act, dt, es in ((B.MOE_SWIGLU, B.MOE_BF16, 2), (B.MOE_SILU, B.MOE_F32, 4)):
-        a = dict(L=3000, d=64, h=200, E=8, K=2, dtype=dt, act=act)
+    """MOE_FLAG_RECOMPUTE_G replaces the [L*K, h] G buffer of the forward and
+    the backward workspace by one [L, h] piece (a slot pass's rows, or a
+    group of experts' routes); unknown flag bits are rejected."""
+    for act, dt, es, K in ((B.MOE_SWIGLU, B.MOE_BF16, 2, 2), (B.MOE_SILU, B.MOE_F32, 4, 3)):
+        a = dict(L=3000, d=64, h=200, E=8, K=K, dtype=dt, act=act)
         base = B.make_shape(**a)
         low = B.make_shape(**a, flags=B.MOE_FLAG_RECOMPUTE_G)
         for n in ("moe_ffn_forward", "moe_ffn_backward"):
             d = B.workspace_bytes(n, base) - B.workspace_bytes(n, low)
-            assert 0 <= d - 3000 * 2 * 200 * es < 256, (n, d)
+            assert abs(d - 3000 * (K - 1) * 200 * es) < 256, (n, d)
         assert B.workspace_bytes("moe_dispatch_build", base) == \
             B.workspace_bytes("moe_dispatch_build", low)
     bad = B.make_shape(**dict(GOOD), flags=2)

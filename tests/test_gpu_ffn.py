@@ -138,9 +138,10 @@ def test_outputs_leave_neighbours_untouched():
         assert torch.all(s[:pad] == 7.0) and torch.all(s[-pad:] == 7.0)
 
 
-# MOE_FLAG_RECOMPUTE_G: no G buffer; the down-projection and dW2 form
-# G = SiLU(A) [* B] (times the gate for dW2) from the checkpoint at operand
-# load, and dW2 runs before the dG kernel replaces A and B.
+# MOE_FLAG_RECOMPUTE_G: no [L*K, h] G buffer; each down-projection pass reads
+# G = SiLU(A) [* B] from an [L, h] piece formed just before it, and dW2 reads
+# gate * G from the same piece, one group of experts (at most L routes) at a
+# time, before the dG kernel replaces A and B.
 RECOMP = [
     (1000, 256, 384, 8, 2, SWIGLU, W.BF16),
     (777, 136, 200, 6, 3, SWIGLU, W.BF16),
@@ -159,13 +160,21 @@ RECOMP = [
                               for a, b, c, e, k, t, u in RECOMP])
 def test_small_full_recompute_g(L, d, h, E, K, act, dt):
     cfg = W.small_config(L, d, h, E, K, act, dt)
-    say(f"  {cfg.name}, G formed at operand load")
+    say(f"  {cfg.name}, G formed in [L, h] pieces")
     run_full_parity(cfg, 11, require_gpu(), recompute_g=True)
+
+
+def test_skewed_small_recompute_g():
+    """Zipf-skewed loads with G formed in pieces: the heaviest expert holds
+    close to L routes, so the dW2 expert groups split around it."""
+    cfg = W.MoEConfig("zipf-small-bf16", 2048, 64, 96, 8, 2, SWIGLU, W.BF16, zipf_skew=True)
+    say(f"  {cfg.name}, G formed in [L, h] pieces")
+    run_full_parity(cfg, 5, require_gpu(), recompute_g=True)
 
 
 @pytest.mark.parametrize("ci", [1, 2])
 def test_configs_full_recompute_g(ci):
-    say(f"  config {ci}, whole tensors, G formed at operand load")
+    say(f"  config {ci}, whole tensors, G formed in [L, h] pieces")
     run_full_parity(W.CONFIGS[ci], ci, require_gpu(), recompute_g=True)
 
 

@@ -784,14 +784,13 @@ __global__ __launch_bounds__(256) void list_bounds(const int32_t* __restrict__ l
   pe_off[i] = (int32_t)(k * L + lo);
 }
 
-// ------------------------------------------------------------------ G at operand load
-// With G not kept (MOE_FLAG_RECOMPUTE_G) the second-layer GEMMs form their
-// operand G = SiLU(A) [* B] (and gate * G for dW2) from the checkpoint as
-// they load it: A and B arrive in registers, G is computed in float32 and
-// rounded once, and the result is written to LDS exactly where a copy of G
-// would have landed.  These loaders use the register path of the main loop
-// (loads in flight during the MFMAs of the current k-tile, LDS writes after
-// them).
+// ------------------------------------------------------------------ G in pieces
+// With G not kept (MOE_FLAG_RECOMPUTE_G) no [L*K, h] buffer exists: before
+// each slot pass of the down-projection its L rows of G = SiLU(A) [* B] are
+// formed from the checkpoint into an [L, h] buffer, and before dW2 the same
+// buffer takes gate * G for one group of experts at a time (at most L
+// routes).  G is computed in float32 from the bf16 (or float32) checkpoint
+// and rounded once.
 
 // 16 bytes of A and B (8 bf16 or 4 float32 each) -> 16 bytes of gate * G.
 template <typename T>
@@ -825,139 +824,63 @@ __device__ __forceinline__ uint4 glu16<float>(uint4 a, uint4 b, bool dual, float
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Rows of G (k contiguous) for the down-projection: the KLoaderD layout,
-// filled from registers.  Row r of the tile is route list[rb + r]; A's row
-// starts at rp[j], B's dB bytes further.
+// G rows formed ahead of a GEMM (MOE_FLAG_RECOMPUTE_G, one piece of at most
+// L rows at a time), 16 bytes per thread:
+//   list != nullptr: out[i] = SiLU(A[p]) [* B[p]], p = list[i], i < n
+//                    (one slot pass's rows);
+//   list == nullptr: out[i] = gate_p[p] * SiLU(A[p]) [* B[p]], p = r0 + i,
+//                    r0 = offsets[chunk_e[c]], up to offsets[chunk_e[c + 1]]
+//                    (the routes of expert group c, contiguous).
+// Block (64, 4): a wavefront covers 64 consecutive chunks of one row; the
+// grid walks the rows in steps (empty groups cost one short pass).
 template <typename T, bool DUAL>
-struct GLULoader {
-  static constexpr bool kDirect = false;
-  static constexpr int RPL = 1024 / ROWB;  // rows per 1 KB load
-  static constexpr int NPL = 32 / RPL;     // loads per thread per k-tile
-  const char* rp[NPL];
-  int64_t dB;
-  int c0, klen;
-  uint4 ra[NPL], rb[NPL];
-
-  __device__ __forceinline__ void setup(const T* A, const T* B, const int32_t* list, int rbeg,
-                                        int rend, int h) {
-    KLoaderD<T> tmp;
-    tmp.init_chunks();
-    c0 = tmp.c0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int li = rbeg + KLoaderD<T>::row_of(j);
-      rp[j] = li < rend ? reinterpret_cast<const char*>(A + (int64_t)list[li] * h) : nullptr;
-    }
-    dB = DUAL ? reinterpret_cast<const char*>(B) - reinterpret_cast<const char*>(A) : 0;
-    klen = h;
+__global__ __launch_bounds__(256) void glu_rows(const T* __restrict__ A, const T* __restrict__ B,
+                                                const int32_t* __restrict__ list,
+                                                const float* __restrict__ gate_p,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ chunk_e, int c,
+                                                int64_t n, int h, T* __restrict__ out) {
+  const int cpr = h * (int)sizeof(T) / 16;  // 16-byte chunks per row (h % 8 == 0)
+  const int q = blockIdx.y * 64 + threadIdx.x;
+  if (q >= cpr) return;
+  int64_t r0 = 0;
+  if (list == nullptr) {
+    r0 = offsets[chunk_e[c]];
+    n = offsets[chunk_e[c + 1]] - r0;
   }
-  // load j of a KLoaderD fetches logical chunk c0 ^ j
-  __device__ __forceinline__ int chunk_of(int j) const { return c0 ^ j; }
-  __device__ __forceinline__ void fetch(int kt) {
-    constexpr int ES = Traits<T>::ES, VEC = Traits<T>::VEC, KT = Traits<T>::KT;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int k = kt * KT + chunk_of(j) * VEC;
-      const bool ok = rp[j] != nullptr && k < klen;
-      const char* g = ok ? rp[j] + (int64_t)k * ES : nullptr;
-      ra[j] = ok ? *reinterpret_cast<const uint4*>(g) : make_uint4(0, 0, 0, 0);
-      rb[j] = (ok && DUAL) ? *reinterpret_cast<const uint4*>(g + dB) : make_uint4(0, 0, 0, 0);
-    }
+  const int64_t rb = (int64_t)h * sizeof(T);  // row bytes
+  for (int64_t i = (int64_t)blockIdx.x * 4 + threadIdx.y; i < n; i += (int64_t)gridDim.x * 4) {
+    const int64_t p = list != nullptr ? (int64_t)list[i] : r0 + i;
+    const int64_t o = p * rb + q * 16;
+    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(A) + o);
+    const uint4 b = DUAL ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(B) + o)
+                         : a;
+    const float g = list != nullptr ? 1.0f : gate_p[p];
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(out) + i * rb + q * 16) =
+        glu16<T>(a, b, DUAL, g);
   }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      *reinterpret_cast<uint4*>(lds + (w * 32 + RPL * j) * ROWB + lane * 16) =
-          glu16<T>(ra[j], rb[j], DUAL, 1.0f);
-  }
-};
+}
 
-// gate * G of the dW2 product, bf16: the TLoaderD layout ([k = route][h
-// position], 512 bytes per k-row) filled from registers; route p = rbase + k
-// (an expert's routes are contiguous), gate gate_p[p].
-template <bool DUAL>
-struct TGLULoader {
-  static constexpr bool kDirect = false;
-  const char* col[4];     // A's column of load j (route 0); absent: nullptr
-  int64_t ld, dB;
-  int64_t rbase;
-  int klen;
-  const float* gate_p;
-  uint4 ra[4], rb[4];
-  float g[4];
-
-  __device__ __forceinline__ void setup(const bf16_t* A, const bf16_t* B, int first_pos,
-                                        int limit, int h, int64_t rbase_, int klen_,
-                                        const float* gate_p_) {
-    ld = (int64_t)h * 2;
-    dB = DUAL ? reinterpret_cast<const char*>(B) - reinterpret_cast<const char*>(A) : 0;
-    rbase = rbase_;
-    klen = klen_;
-    gate_p = gate_p_;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = first_pos + TLoaderD::lpos(j);
-      col[j] = p < limit ? reinterpret_cast<const char*>(A) + (int64_t)p * 2 : nullptr;
+// Expert groups for dW2 under MOE_FLAG_RECOMPUTE_G: consecutive experts
+// whose routes total at most cap = L, taken greedily from expert 0 (one
+// expert alone never exceeds L).  Two neighbouring groups hold more than L
+// routes together, so R = K L routes make at most 2K + 1 groups.
+// chunk_e[g] is the first expert of group g; unused entries up to
+// chunk_e[NC] are E (empty groups).
+__global__ void glu_chunks(const int32_t* __restrict__ offsets, int E, int64_t cap, int NC,
+                           int32_t* __restrict__ chunk_e) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int g = 0;
+  chunk_e[0] = 0;
+  int64_t start = offsets[0];
+  for (int e = 0; e < E; ++e) {
+    if ((int64_t)offsets[e + 1] - start > cap && g + 1 < NC) {
+      chunk_e[++g] = e;
+      start = offsets[e];
     }
   }
-  __device__ __forceinline__ void fetch(int kt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = kt * 64 + TLoaderD::krow(j);
-      const bool ok = col[j] != nullptr && k < klen;
-      const char* a = ok ? col[j] + (rbase + k) * ld : nullptr;
-      ra[j] = ok ? *reinterpret_cast<const uint4*>(a) : make_uint4(0, 0, 0, 0);
-      rb[j] = (ok && DUAL) ? *reinterpret_cast<const uint4*>(a + dB) : make_uint4(0, 0, 0, 0);
-      g[j] = k < klen ? gate_p[rbase + k] : 0.f;
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(lds + (w * 8 + 2 * j) * 512 + lane * 16) =
-          glu16<bf16_t>(ra[j], rb[j], DUAL, g[j]);
-  }
-};
-
-// gate * G of the dW2 product, float32: the MNLoader layout (positions
-// contiguous in memory, transposed in registers on the way into LDS).
-template <bool DUAL>
-struct MNGLULoader {
-  static constexpr bool kDirect = false;
-  MNLoader<float> a, b;
-  const float* gate_p;
-  int64_t rbase;
-  int klen;
-  float g[4];
-
-  __device__ __forceinline__ void setup(const float* A, const float* B, int first_pos, int limit,
-                                        int h, int64_t rbase_, int klen_, const float* gate_p_) {
-    a.setup(reinterpret_cast<const char*>(A), first_pos, limit, (int64_t)h * 4, nullptr, rbase_,
-            klen_);
-    if (DUAL)
-      b.setup(reinterpret_cast<const char*>(B), first_pos, limit, (int64_t)h * 4, nullptr, rbase_,
-              klen_);
-    gate_p = gate_p_;
-    rbase = rbase_;
-    klen = klen_;
-  }
-  __device__ __forceinline__ void fetch(int kt) {
-    a.fetch(kt);
-    if (DUAL) b.fetch(kt);
-    const int k0 = kt * Traits<float>::KT + MNLoader<float>::krow0();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) g[i] = k0 + i < klen ? gate_p[rbase + k0 + i] : 0.f;
-  }
-  __device__ __forceinline__ void store(char* lds) {
-    // a.reg[i] holds 4 positions of k-row k0 + i: apply gate * SiLU(A) [* B]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a.reg[i] = glu16<float>(a.reg[i], DUAL ? b.reg[i] : make_uint4(0, 0, 0, 0), DUAL, g[i]);
-    a.store(lds);
-  }
-};
+  for (int j = g + 1; j <= NC; ++j) chunk_e[j] = E;
+}
 
 // ------------------------------------------------------------------ kernels
 
@@ -1277,19 +1200,19 @@ __device__ __forceinline__ void combine_dispatch(const Acc& acc, char* smem, con
 }
 
 // F2 (slot pass k): O = G W2_e for the pass's rows, y[t] (+)= gate * O.
-// W2T: [E, d, h] (transposed weights).  GM = 0: G read from Gb; GM = 1 / 2:
-// G = SiLU(A) / SiLU(A) * B formed from the checkpoint at operand load.
+// W2T: [E, d, h] (transposed weights).  GM = 0: G read from Gb, row list[li];
+// GM = 3: Gb holds only this pass's rows, row li - pbase (list position
+// relative to the pass).
 template <typename T, int GM>
 __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* __restrict__ Gb,
-                                                         const T* __restrict__ Ab,
-                                                         const T* __restrict__ Bb,
                                                          const T* __restrict__ W2T,
                                                          const int32_t* __restrict__ list,
                                                          const int32_t* __restrict__ eti,
                                                          const float* __restrict__ gates, int K,
                                                          int k, int d, int h, int mode,
-                                                         T* __restrict__ y,
+                                                         int64_t pbase, T* __restrict__ y,
                                                          float* __restrict__ yacc) {
+  static_assert(GM == 0 || GM == 3, "G read from the full buffer or from the pass's piece");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   __shared__ int32_t s_t[TBM];
   __shared__ float s_g[TBM];
@@ -1316,17 +1239,14 @@ __global__ __launch_bounds__(NT, 1) void f2_down_combine(RouteArgs ra, const T* 
   lb.delta = 0;
   lb.ksplit = lb.klen = h;
   Acc acc;
-  if constexpr (GM == 0) {
-    KLoaderD<T> la;
+  KLoaderD<T> la;
+  if constexpr (GM == 0)
     kloaderd_rows<T>(la, Gb, list, nullptr, rb, re, h, ra.zero);
-    la.delta = 0;
-    la.ksplit = la.klen = h;
-    gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
-  } else {
-    GLULoader<T, GM == 2> la;
-    la.setup(Ab, Bb, list, rb, re, h);
-    gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
-  }
+  else
+    kloaderd_rows<T>(la, Gb, nullptr, nullptr, (int)(rb - pbase), (int)(re - pbase), h, ra.zero);
+  la.delta = 0;
+  la.ksplit = la.klen = h;
+  gemm_mainloop<T>(la, lb, (h + KT - 1) / KT, smem, acc);
   __syncthreads();
   combine_dispatch<T>(acc, smem, s_t, s_g, re - rb, n0, d, mode, y, yacc);
 }
@@ -1546,22 +1466,29 @@ __device__ __forceinline__ bool weight_tile(const WeightArgs& wa, int& e, int& m
 }
 
 // B0: dW2_e = Gs_e^T dy_e (reduction over the expert's routes, ascending).
-// GM = 0: Gs = gate * G read from the buffer the dG kernel wrote; GM = 1 / 2:
-// formed at operand load from the checkpoint A [, B] and the route gates
-// (this kernel then runs before the dG kernel replaces A and B).
+// GM = 0: Gs = gate * G read from the buffer the dG kernel wrote; GM = 3:
+// Gs holds only the routes of expert group c (experts chunk_e[c] ..
+// chunk_e[c + 1] - 1, from route offsets[chunk_e[c]] on), formed from A, B
+// before the dG kernel replaces them, and the other experts' workgroups
+// return.
 template <typename T, int GM>
 __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restrict__ Gs,
-                                                const T* __restrict__ Ab,
-                                                const T* __restrict__ Bb,
-                                                const float* __restrict__ gate_p,
                                                 const T* __restrict__ dy,
                                                 const int32_t* __restrict__ eti,
                                                 const int32_t* __restrict__ offsets, int d, int h,
+                                                const int32_t* __restrict__ chunk_e, int c,
                                                 T* __restrict__ dW2) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  static_assert(GM == 0 || GM == 3, "gate * G from the full buffer or from a group's piece");
   constexpr int ES = Traits<T>::ES, KT = Traits<T>::KT;
   int e, mi, ni;
   if (!weight_tile(wa, e, mi, ni)) return;
+  int gbase = 0;  // first route held in Gs
+  if constexpr (GM == 3) {
+    const int e0 = chunk_e[c], e1 = chunk_e[c + 1];
+    if (e < e0 || e >= e1) return;
+    gbase = offsets[e0];
+  }
   const int m0 = mi * 256, n0 = ni * 256;
   const int o0 = offsets[e], n_e = offsets[e + 1] - o0;
   // with h % 256 == 128 the last M tile's second row half is padding
@@ -1572,30 +1499,17 @@ __global__ __launch_bounds__(NT, 1) void b0_dw2(WeightArgs wa, const T* __restri
     TLoaderD lb;
     lb.setup<false>(reinterpret_cast<const char*>(dy), nullptr, n0, d, (int64_t)d * ES, eti + o0,
                     0, n_e, wa.zero);
-    if constexpr (GM == 0) {
-      TLoaderD la;
-      la.setup<false>(reinterpret_cast<const char*>(Gs), nullptr, m0, h, (int64_t)h * ES, nullptr,
-                      o0, n_e, wa.zero);
-      gemm_mainloop<T, TLoaderD, TLoaderD, true, false, true>(la, lb, (n_e + KT - 1) / KT, smem,
-                                                              acc, live);
-    } else {
-      TGLULoader<GM == 2> la;
-      la.setup(Ab, Bb, m0, h, h, o0, n_e, gate_p);
-      gemm_mainloop<T, TGLULoader<GM == 2>, TLoaderD, true>(la, lb, (n_e + KT - 1) / KT, smem,
-                                                             acc);
-    }
+    TLoaderD la;
+    la.setup<false>(reinterpret_cast<const char*>(Gs), nullptr, m0, h, (int64_t)h * ES, nullptr,
+                    o0 - gbase, n_e, wa.zero);
+    gemm_mainloop<T, TLoaderD, TLoaderD, true, false, true>(la, lb, (n_e + KT - 1) / KT, smem, acc,
+                                                            live);
   } else {
     MNLoader<T> lb;
     lb.setup(reinterpret_cast<const char*>(dy), n0, d, (int64_t)d * ES, eti + o0, 0, n_e);
-    if constexpr (GM == 0) {
-      MNLoader<T> la;
-      la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0, n_e);
-      gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
-    } else {
-      MNGLULoader<GM == 2> la;
-      la.setup(Ab, Bb, m0, h, h, o0, n_e, gate_p);
-      gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
-    }
+    MNLoader<T> la;
+    la.setup(reinterpret_cast<const char*>(Gs), m0, h, (int64_t)h * ES, nullptr, o0 - gbase, n_e);
+    gemm_mainloop<T>(la, lb, (n_e + KT - 1) / KT, smem, acc);
   }
 
   T* out = dW2 + (int64_t)e * h * d;
@@ -1734,8 +1648,11 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   const bool need_acc = dm.dtype == 1 && dm.K > 1;
   const size_t wbytes = (size_t)dm.E * dm.d * dm.h * es;
   size_t o = 0;
-  // G (forward) or gate * G (backward), unless the second GEMMs form it from A, B
-  p.off_g = o;      o = align_up(o + (dm.recompute_g ? 0 : (size_t)p.R * dm.h * es), 256);
+  // G (forward) or gate * G (backward) for all R routes; with recompute_g
+  // one piece of at most L rows at a time (a slot pass's rows, or a group of
+  // experts: an expert has at most one route per token)
+  p.off_g = o;
+  o = align_up(o + (size_t)(dm.recompute_g ? dm.L : p.R) * dm.h * es, 256);
   p.off_acc = o;    o = align_up(o + (need_acc ? (size_t)dm.L * dm.d * 4 : 0), 256);
   p.off_slot = o;   o = align_up(o + (size_t)p.R + 16, 256);
   p.off_list = o;   o = align_up(o + (size_t)p.R * 4, 256);
@@ -1750,6 +1667,8 @@ FfnPlan plan_ffn(const FfnDims& dm, bool backward) {
   const int nW = backward ? 0 : (dm.act == 1 ? 3 : 2);   // W1T, W2T, (W3T)
   p.off_wt = o;     o = align_up(o + nW * wbytes, 256);
   p.off_zero = o;   o = align_up(o + 256, 256);
+  p.n_chunk = dm.recompute_g && backward ? 2 * dm.K + 1 : 0;
+  p.off_chunk = o;  o = align_up(o + (size_t)(p.n_chunk + 1) * 4, 256);
   p.bytes = o;
   return p;
 }
@@ -1812,6 +1731,23 @@ static void transpose_w(const T* W, T* WT, int E, int R, int C, hipStream_t s) {
                      dim3(256), 0, s, W, WT, R, C);
 }
 
+// G rows ahead of a GEMM (see glu_rows); nmax bounds the rows (n is read on
+// the device for expert groups).
+template <typename T>
+static void glu_launch(bool dual, const T* A, const T* B, const int32_t* list,
+                       const float* gate_p, const int32_t* offsets, const int32_t* chunk_e, int c,
+                       int64_t nmax, int h, T* out, hipStream_t s) {
+  const int cpr = h * (int)sizeof(T) / 16;
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(nmax, 4), 16384)),
+                  (unsigned)cdiv(cpr, 64));
+  if (dual)
+    hipLaunchKernelGGL((glu_rows<T, true>), grid, dim3(64, 4), 0, s, A, B, list, gate_p, offsets,
+                       chunk_e, c, nmax, h, out);
+  else
+    hipLaunchKernelGGL((glu_rows<T, false>), grid, dim3(64, 4), 0, s, A, B, list, gate_p, offsets,
+                       chunk_e, c, nmax, h, out);
+}
+
 template <typename T>
 static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T* W1, const T* W3,
                       const T* W2, const int32_t* eti, const int32_t* offsets, const int32_t* tim,
@@ -1846,15 +1782,23 @@ static void forward_t(const FfnPlan& pl, const FfnDims& dm, const T* x, const T*
     }
 #undef MOE_F1
   }
-  const int gm = keepg ? 0 : (dual ? 2 : 1);
+  // G kept: F1 wrote it for every route.  Not kept: before each pass, the
+  // pass's L rows of G are formed from A, B into the same buffer.
+  const int gm = keepg ? 0 : 3;
   for (int k = 0; k < dm.K; ++k) {
+    if (!keepg) {
+      LaunchTimer lt("glu_transient", s);
+      glu_launch<T>(dual, A, B, ls.list + (int64_t)k * dm.L, nullptr, nullptr, nullptr, 0, dm.L,
+                    dm.h, G, s);
+    }
     LaunchTimer lt("ffn_f2_down_combine", s);
     RouteArgs ra{ls.tiles_pass + (int64_t)k * pl.pass_tiles, pl.pass_tiles, (int)cdiv(dm.d, 256), (const char*)ls.zero, 1};
     const unsigned grid = (unsigned)route_grid(ra);
 #define MOE_F2(GMV)                                                                             \
-  hipLaunchKernelGGL((f2_down_combine<T, GMV>), dim3(grid), dim3(NT), 0, s, ra, G, A, B, W2T,     \
-                     ls.list, eti, gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32), y, acc)
-    if (gm == 0) MOE_F2(0); else if (gm == 1) MOE_F2(1); else MOE_F2(2);
+  hipLaunchKernelGGL((f2_down_combine<T, GMV>), dim3(grid), dim3(NT), 0, s, ra, G, W2T,           \
+                     ls.list, eti, gates, dm.K, k, dm.d, dm.h, pass_mode(dm.K, k, f32),           \
+                     (int64_t)k * dm.L, y, acc)
+    if (gm == 0) MOE_F2(0); else MOE_F2(3);
 #undef MOE_F2
   }
 }
@@ -1869,21 +1813,38 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   float* gate_p = reinterpret_cast<float*>(ws + pl.off_gatep);
   Lists ls = build_lists(pl, dm, offsets, tim, gates, gate_p, ws, s);
   T* Gs = reinterpret_cast<T*>(ws + pl.off_g);
+  int32_t* chunk_e = reinterpret_cast<int32_t*>(ws + pl.off_chunk);
   float* acc = f32 ? reinterpret_cast<float*>(dx) : reinterpret_cast<float*>(ws + pl.off_acc);
   float* dgp = dlogits != nullptr ? reinterpret_cast<float*>(ws + pl.off_dgp) : nullptr;
   const int nNh = (int)cdiv(dm.h, 256);
   const bool keepg = !dm.recompute_g;
-  const int gm = keepg ? 0 : (dual ? 2 : 1);
-  // dW2 needs gate * G: from the dG kernel's buffer (after it), or formed
-  // from A, B (before the dG kernel writes dA, dB over them)
+  // dW2 needs gate * G: from the dG kernel's buffer (after it), or, not kept,
+  // formed from A, B (before the dG kernel writes dA, dB over them) one
+  // expert group of at most L routes at a time into the same buffer
   auto dw2 = [&]() {
-    LaunchTimer lt("ffn_b0_dw2", s);
     WeightArgs wa{dm.E, (int)cdiv(dm.h, 256), (int)cdiv(dm.d, 256), (const char*)ls.zero};
     const int64_t n = (int64_t)dm.E * wa.nM * wa.nN;
-#define MOE_B0(GMV)                                                                             \
-  hipLaunchKernelGGL((b0_dw2<T, GMV>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, A, B,    \
-                     gate_p, dy, eti, offsets, dm.d, dm.h, dW2)
-    if (gm == 0) MOE_B0(0); else if (gm == 1) MOE_B0(1); else MOE_B0(2);
+#define MOE_B0(GMV, C)                                                                          \
+  hipLaunchKernelGGL((b0_dw2<T, GMV>), dim3((unsigned)round8(n)), dim3(NT), 0, s, wa, Gs, dy, eti, \
+                     offsets, dm.d, dm.h, chunk_e, C, dW2)
+    if (keepg) {
+      LaunchTimer lt("ffn_b0_dw2", s);
+      MOE_B0(0, 0);
+      return;
+    }
+    {
+      LaunchTimer lt("glu_transient", s);
+      hipLaunchKernelGGL(glu_chunks, dim3(1), dim3(64), 0, s, offsets, dm.E, dm.L, pl.n_chunk,
+                         chunk_e);
+    }
+    for (int c = 0; c < pl.n_chunk; ++c) {
+      {
+        LaunchTimer lt("glu_transient", s);
+        glu_launch<T>(dual, A, B, nullptr, gate_p, offsets, chunk_e, c, dm.L, dm.h, Gs, s);
+      }
+      LaunchTimer lt("ffn_b0_dw2", s);
+      MOE_B0(3, c);
+    }
 #undef MOE_B0
   };
   if (!keepg) dw2();

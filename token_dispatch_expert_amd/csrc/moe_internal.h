@@ -41,7 +41,7 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
 struct FfnDims {
   int64_t L;
   int d, h, E, K, dtype, act;
-  bool recompute_g;  // no G buffer: the second GEMMs form G from A, B
+  bool recompute_g;  // no G buffer: G (gate * G) formed from A, B in L-row pieces
 };
 
 struct FfnPlan {
@@ -50,7 +50,8 @@ struct FfnPlan {
   int64_t pass_tiles;    // upper bound of M tiles per slot pass
   int64_t list_chunks;   // chunks of the slot-list builder
   size_t off_g, off_acc, off_slot, off_list, off_cnt, off_base, off_peoff, off_gatep, off_dgp;
-  size_t off_tiles_route, off_tiles_pass, off_wt, off_zero, bytes;
+  size_t off_tiles_route, off_tiles_pass, off_wt, off_zero, off_chunk, bytes;
+  int n_chunk;           // expert groups of dW2 under recompute_g (at most 2K + 1)
 };
 FfnPlan plan_ffn(const FfnDims& dm, bool backward);
 
