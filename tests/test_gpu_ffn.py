@@ -94,13 +94,16 @@ def test_large_configs_sampled(ci):
     run_sampled_parity(W.CONFIGS[ci], ci, require_gpu())
 
 
-def test_bitwise_repeatable_and_poisoned_workspace():
+@pytest.mark.parametrize("recompute_g", [False, True], ids=["keep_g", "recompute_g"])
+def test_bitwise_repeatable_and_poisoned_workspace(recompute_g):
+    """Three runs (workspace untouched, all 0xFF, all 0x00) give bitwise equal
+    outputs, in both G modes."""
     dev = require_gpu()
     cfg = W.small_config(3000, 256, 384, 8, 3, SWIGLU, W.BF16)
     inp = W.make_inputs(cfg, 21, dev)
     outs = []
     for poison in (None, 0xFF, 0x00):
-        buf = MoELayerBuffers(cfg, dev, router_grad=True)
+        buf = MoELayerBuffers(cfg, dev, router_grad=True, recompute_g=recompute_g)
         if poison is not None:
             buf.ws.fill_(poison)
         buf.build(inp["logits"])
