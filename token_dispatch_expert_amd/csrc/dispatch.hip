@@ -655,25 +655,46 @@ __global__ __launch_bounds__(64) void k1_route_wide_mask(
     src.abase = lbase - src.mis;
     src.end16 = (src.mis + L * rowb + 15) & ~(int64_t)15;
   }
+  // E == 64 P (every lane owns 64 experts) with 16-byte aligned rows and
+  // L >= TPR: a round is exactly 16 KB, read through registers (sixteen
+  // coalesced 16-byte loads per lane) and written to LDS by the wavefront;
+  // the last round reads rows [L - TPR, L) so every load is in range.
+  // Otherwise direct-to-LDS copies.
+  const bool regpath = VEC && E == 64 * P && L >= TPR;
   for (int rd = 0; rd < P; ++rd) {
     const int64_t tr0 = part * 64 + (int64_t)rd * TPR;   // first token of the round
-    const int64_t first = src.mis + tr0 * rowb;
-    const int64_t first16 = first & ~(int64_t)15;
-    const int delta = (int)(first - first16);
-    const int nq = tr0 < L ? (int)((delta + (int64_t)TPR * rowb + 1023) >> 10) : 0;
-    // the previous round's LDS reads are done before its stage is rewritten
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int c = 0; c < nq; ++c) {
-      const int64_t off = first16 + (int64_t)c * 1024 + lane * 16;
-      const char* g = src.abase + (off + 16 <= src.end16 ? off : 0);
-      __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(stage + c * 1024), 16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-
     const int64_t t = tr0 + i;
     const bool live = t < L;
-    const float* row = reinterpret_cast<const float*>(stage + delta + (int64_t)i * rowb) + e0;
+    const float* row;
+    if (regpath) {
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      const int64_t fr = min(tr0, L - TPR);  // first row of the round's copy
+      const v4f* pb = reinterpret_cast<const v4f*>(logits) + fr * (E >> 2);  // uniform
+      v4f vv[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) vv[c] = __builtin_nontemporal_load(pb + c * 64 + lane);
+      // (the previous round's LDS reads come first in program order)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) reinterpret_cast<v4f*>(stage)[c * 64 + lane] = vv[c];
+      __builtin_amdgcn_wave_barrier();
+      const int srow = (int)min<int64_t>(t - fr, TPR - 1);  // rows past L: any row
+      row = reinterpret_cast<const float*>(stage + (int64_t)srow * rowb) + e0;
+    } else {
+      const int64_t first = src.mis + tr0 * rowb;
+      const int64_t first16 = first & ~(int64_t)15;
+      const int delta = (int)(first - first16);
+      const int nq = tr0 < L ? (int)((delta + (int64_t)TPR * rowb + 1023) >> 10) : 0;
+      // the previous round's LDS reads are done before its stage is rewritten
+      __builtin_amdgcn_s_waitcnt(0);
+      for (int c = 0; c < nq; ++c) {
+        const int64_t off = first16 + (int64_t)c * 1024 + lane * 16;
+        const char* g = src.abase + (off + 16 <= src.end16 ? off : 0);
+        __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(stage + c * 1024), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      row = reinterpret_cast<const float*>(stage + delta + (int64_t)i * rowb) + e0;
+    }
     auto chunk = [&](int c, float (&v)[4]) {
       if (VEC && 4 * c + 4 <= ne) {
         const float4 x = reinterpret_cast<const float4*>(row)[c];
