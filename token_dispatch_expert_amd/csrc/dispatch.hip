@@ -838,7 +838,7 @@ __global__ __launch_bounds__(64) void k1_route_wide_mask(
 // rows leave as one contiguous run.  Expert-indexed work (segment starts,
 // running bases, run starts) is spread over the 256 threads, EPT
 // consecutive experts each.
-template <int W>
+template <int W, int KMAX>
 __global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restrict__ tmask,
                                                        const uint64_t* __restrict__ tcol,
                                                        int64_t L, int E, int K, int NU,
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restric
                                                        int32_t* __restrict__ tim) {
   constexpr int EM = 64 * W;
   constexpr int EPT = (EM + 255) / 256;  // experts per thread
-  constexpr int MAXE = 256 * 8;          // entries of one tile (K <= 8)
+  constexpr int MAXE = 256 * KMAX;       // entries of one tile (K <= KMAX), sized as in k3_scatter_mask
   __shared__ int s_off[EM + 1];
   __shared__ int scratch[4];
   __shared__ uint64_t s_col[4][EM];
@@ -1267,9 +1267,16 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
     LaunchTimer lt("dispatch_scatter", s);
     const uint64_t* tmask = reinterpret_cast<const uint64_t*>(ws + pl.off_map);
     const uint64_t* tcol = reinterpret_cast<const uint64_t*>(ws + pl.off_col);
+#define K3WK(WV, KX)                                                                            \
+  hipLaunchKernelGGL((k3_scatter_wide<WV, KX>), dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K, \
+                     pl.C, base, total, eti, offsets, tim)
 #define K3W(WV)                                                                                 \
-  hipLaunchKernelGGL(k3_scatter_wide<WV>, dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K, pl.C, \
-                     base, total, eti, offsets, tim)
+  do {                                                                                          \
+    if (K <= 2) K3WK(WV, 2);                                                                    \
+    else if (K <= 4) K3WK(WV, 4);                                                               \
+    else if (K <= 6) K3WK(WV, 6);                                                               \
+    else K3WK(WV, 8);                                                                           \
+  } while (0)
 #define K3M(KX)                                                                                 \
   hipLaunchKernelGGL((k3_scatter_mask<4, KX>), dim3(pl.C), dim3(256), 0, s, tmask, tcol, L, E, K,  \
                      pl.C, base, total, eti, offsets, tim)
@@ -1288,6 +1295,7 @@ hipError_t launch_dispatch(const DispatchPlan& pl, int64_t L, int E, int K, cons
     else if (pl.stream)
       K3W(16);
 #undef K3W
+#undef K3WK
 #undef K3M
     else
       hipLaunchKernelGGL(k3_scatter, dim3(pl.C), dim3(256), 0, s, map, pl.Lpad, E, K, pl.T, pl.C,
