@@ -1396,14 +1396,14 @@ __global__ __launch_bounds__(NT, 1) void b1_dgrad_glu(RouteArgs ra, const T* __r
 // the selected logits, dz_k = g_k (dg_k - sum_j g_j dg_j), sum in ascending
 // k, in place; then the workgroup writes the TB full rows of dlogits (zeros
 // for experts not chosen).
-constexpr int kRouterRows = 16384;  // floats of LDS: TB rows of E
+constexpr int kRouterRows = 16384;  // floats of LDS at most: TB rows of E (dynamic, TB * E used)
 __global__ __launch_bounds__(256) void router_grad(const int32_t* __restrict__ tei,
                                                    const int32_t* __restrict__ tim,
                                                    const float* __restrict__ gates,
                                                    const float* __restrict__ dgp, int nN,
                                                    int64_t L, int E, int K, int TB,
                                                    float* __restrict__ dz) {
-  __shared__ float s_rows[kRouterRows];
+  extern __shared__ float s_rows[];  // TB * E floats, sized at launch
   const int64_t t0 = (int64_t)blockIdx.x * TB;
   const int nrow = (int)min<int64_t>(TB, L - t0);
   for (int i = threadIdx.x; i < nrow * E; i += 256) s_rows[i] = 0.f;
@@ -1870,8 +1870,9 @@ static void backward_t(const FfnPlan& pl, const FfnDims& dm, const T* dy, const 
   if (dlogits != nullptr) {
     LaunchTimer lt("router_grad", s);
     const int TB = std::min(64, kRouterRows / dm.E);
-    hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, TB)), dim3(256), 0, s, tei, tim,
-                       gates, dgp, nNh, dm.L, dm.E, dm.K, TB, dlogits);
+    hipLaunchKernelGGL(router_grad, dim3((unsigned)cdiv(dm.L, TB)), dim3(256),
+                       (size_t)TB * dm.E * sizeof(float), s, tei, tim, gates, dgp, nNh, dm.L, dm.E,
+                       dm.K, TB, dlogits);
   }
   if (keepg) dw2();
   {
