@@ -506,7 +506,12 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
   __shared__ int s_base[4][64];
   __shared__ int s_run[65];  // start of each expert's run inside the tile
   __shared__ int s_tok[MAXE];
-  __shared__ int s_pos[MAXE];
+  // expert of each staged entry; its position in expert_token_indices is the
+  // entry's index plus s_dl[e] (the tile's run of e lies in one run of e's
+  // segment), which saves a 4-byte position per entry: 8 workgroups per CU
+  // at K = 6 instead of 6
+  __shared__ uint8_t s_ex[MAXE];
+  __shared__ int s_dl[64];
   __shared__ int s_tim[MAXE];  // the tile's token_index_map rows, written out contiguously
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -553,6 +558,7 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
     const int n = lane < E ? run - first : 0;  // this tile's tokens of expert lane
     const int incl = wave_incl_scan(n, lane);
     if (lane < E) s_run[lane] = incl - n;
+    s_dl[lane] = lane < E ? first - (incl - n) : 0;
     if (lane == 63) s_run[64] = incl;
   }
   __syncthreads();
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
         const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
         if (lp < MAXE) {  // always true when the masks hold K bits each
           s_tok[lp] = (int32_t)t;
-          s_pos[lp] = pos;
+          s_ex[lp] = (uint8_t)e;
         }
       }
       s_tim[tid * K + k] = pos;
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
 #pragma unroll
   for (int u = 0; u < NJ; ++u) {
     const int j = min(tid + u * 256, MAXE - 1);
-    pv[u] = s_pos[j];
+    pv[u] = j + s_dl[s_ex[j] & 63];  // entries past n are not stored
     tv[u] = s_tok[j];
   }
 #pragma unroll
@@ -850,13 +856,16 @@ __global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restric
   constexpr int EM = 64 * W;
   constexpr int EPT = (EM + 255) / 256;  // experts per thread
   constexpr int MAXE = 256 * KMAX;       // entries of one tile (K <= KMAX), sized as in k3_scatter_mask
+  static_assert((EM & (EM - 1)) == 0, "expert ids of staged entries are masked with EM - 1");
   __shared__ int s_off[EM + 1];
   __shared__ int scratch[4];
   __shared__ uint64_t s_col[4][EM];
   __shared__ int s_base[4][EM];
   __shared__ int s_run[EM + 1];
   __shared__ int s_tok[MAXE];
-  __shared__ int s_pos[MAXE];
+  // expert of each staged entry: the entry's position in
+  // expert_token_indices is its index plus s_base[0][e] - s_run[e]
+  __shared__ uint16_t s_ex[MAXE];
   __shared__ int s_tim[MAXE];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -940,7 +949,7 @@ __global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restric
         const int lp = s_run[e] + (s_base[wave][e] - s_base[0][e]) + below;
         if (lp < MAXE) {  // always true when the masks hold K bits each
           s_tok[lp] = (int32_t)t;
-          s_pos[lp] = pos;
+          s_ex[lp] = (uint16_t)e;
         }
       }
       s_tim[tid * K + k] = pos;
@@ -954,7 +963,8 @@ __global__ __launch_bounds__(256) void k3_scatter_wide(const uint64_t* __restric
 #pragma unroll
   for (int u = 0; u < NJ; ++u) {
     const int j = min(tid + u * 256, MAXE - 1);
-    pv[u] = s_pos[j];
+    const int e = s_ex[j] & (EM - 1);  // entries past nrun are not stored
+    pv[u] = j + s_base[0][e] - s_run[e];
     tk[u] = s_tok[j];
   }
 #pragma unroll
