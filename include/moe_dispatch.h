@@ -20,7 +20,11 @@
  *     HIP device, row-major and contiguous.  The caller owns every buffer; the
  *     library never allocates, frees or synchronises.  All work is enqueued on
  *     `stream` (a hipStream_t; NULL = the null stream) and the call returns
- *     before it runs.
+ *     before it runs.  A call launches kernels only (no copy, no memset; no
+ *     event either while the kernel timers of moe_profile_enable are off, the
+ *     default), so a sequence of calls can be captured into a HIP graph on a
+ *     capturing stream and replayed; the graph keeps the pointers it was
+ *     captured with.
  *   - Workspace: pass ws == NULL to query; the required size is written to
  *     *ws_bytes, MOE_OK is returned and nothing is launched.  Otherwise
  *     *ws_bytes is the size of `ws` (device memory, 256-byte aligned); if it is
