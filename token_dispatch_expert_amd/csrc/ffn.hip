@@ -849,15 +849,32 @@ __global__ __launch_bounds__(256) void glu_rows(const T* __restrict__ A, const T
     n = offsets[chunk_e[c + 1]] - r0;
   }
   const int64_t rb = (int64_t)h * sizeof(T);  // row bytes
-  for (int64_t i = (int64_t)blockIdx.x * 4 + threadIdx.y; i < n; i += (int64_t)gridDim.x * 4) {
-    const int64_t p = list != nullptr ? (int64_t)list[i] : r0 + i;
-    const int64_t o = p * rb + q * 16;
-    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(A) + o);
-    const uint4 b = DUAL ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(B) + o)
-                         : a;
-    const float g = list != nullptr ? 1.0f : gate_p[p];
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(out) + i * rb + q * 16) =
-        glu16<T>(a, b, DUAL, g);
+  // U rows per thread and sweep, every load out before the first store
+  constexpr int U = 4;
+  const int64_t S = (int64_t)gridDim.x * 4;
+  for (int64_t i0 = (int64_t)blockIdx.x * 4 + threadIdx.y; i0 < n; i0 += S * U) {
+    int64_t p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = min(i0 + u * S, n - 1);  // rows past n repeat row n - 1, not stored
+      p[u] = list != nullptr ? (int64_t)list[i] : r0 + i;
+    }
+    uint4 a[U], b[U];
+    float g[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = p[u] * rb + q * 16;
+      a[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(A) + o);
+      b[u] = DUAL ? *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(B) + o) : a[u];
+      g[u] = list != nullptr ? 1.0f : gate_p[p[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * S;
+      if (i < n)
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(out) + i * rb + q * 16) =
+            glu16<T>(a[u], b[u], DUAL, g[u]);
+    }
   }
 }
 
@@ -1738,7 +1755,7 @@ static void glu_launch(bool dual, const T* A, const T* B, const int32_t* list,
                        const float* gate_p, const int32_t* offsets, const int32_t* chunk_e, int c,
                        int64_t nmax, int h, T* out, hipStream_t s) {
   const int cpr = h * (int)sizeof(T) / 16;
-  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(nmax, 4), 16384)),
+  const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(nmax, 16), 16384)),
                   (unsigned)cdiv(cpr, 64));
   if (dual)
     hipLaunchKernelGGL((glu_rows<T, true>), grid, dim3(64, 4), 0, s, A, B, list, gate_p, offsets,
