@@ -127,3 +127,70 @@ def test_dispatch_repeatable():
     torch.cuda.synchronize()
     for n in ("eti", "offsets", "tei", "tim", "gates"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+
+
+def test_dispatch_max_size():
+    """The largest routing the ABI accepts at K = 8: L = 2^28 - 1 tokens
+    (L * K = 2^31 - 8 routes, the last 64-token part ragged), E = 16.  The
+    oracle routes a sample of tokens one by one (their expert lists bit-exact,
+    gates within 1e-6); everything else is checked through properties that
+    fix it uniquely at any size: token_expert_indices rows strictly ascending
+    and in range, per-expert counts equal to the offsets, each segment of
+    expert_token_indices strictly ascending (so it is the sorted token list),
+    and expert_token_indices[token_index_map[t, k]] = t with
+    token_index_map[t, k] inside the segment of token_expert_indices[t, k]."""
+    import oracle
+    from token_dispatch_expert_amd import binding as B
+
+    dev = require_gpu()
+    E, K = 16, 8
+    L = (2 ** 31 - 1) // K
+    R = L * K
+    say(f"  dispatch L={L} E={E} K={K} (L*K = {R})")
+    g = torch.Generator(device=dev).manual_seed(2024)
+    z = torch.randn(L, E, generator=g, device=dev, dtype=torch.float32)
+    i32 = dict(dtype=torch.int32, device=dev)
+    eti = torch.empty(R, **i32)
+    off = torch.empty(E + 1, **i32)
+    tei = torch.empty(L, K, **i32)
+    tim = torch.empty(L, K, **i32)
+    gates = torch.empty(L, K, dtype=torch.float32, device=dev)
+    shape = B.make_shape(L, 8, 8, E, K)
+    B.moe_dispatch_build(shape, z, eti, off, tei, tim, gates)
+    torch.cuda.synchronize()
+
+    offs = off.cpu().numpy().astype(np.int64)
+    assert offs[0] == 0 and offs[E] == R and np.all(np.diff(offs) >= 0)
+    # sampled tokens against the oracle (first, last and 4,096 random ones)
+    gen = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L),
+                                     gen.integers(0, L, 4096)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    ref_tei, ref_gates = oracle.route(z[ridx].cpu().numpy(), K)
+    assert np.array_equal(tei[ridx].cpu().numpy(), ref_tei), "sampled token_expert_indices"
+    gerr = float(np.abs(gates[ridx].cpu().numpy().astype(np.float64) - ref_gates).max())
+    assert gerr <= 1e-6, gerr
+    # whole-tensor properties, in chunks of tokens
+    counts = torch.zeros(E, dtype=torch.int64, device=dev)
+    offd = off.to(torch.int64)
+    step = 1 << 25
+    for t0 in range(0, L, step):
+        t1 = min(L, t0 + step)
+        te = tei[t0:t1].to(torch.int64)
+        assert bool((te >= 0).all()) and bool((te < E).all())
+        assert bool((te[:, 1:] > te[:, :-1]).all()), "a token's experts not ascending"
+        counts += torch.bincount(te.reshape(-1), minlength=E)
+        tm = tim[t0:t1].to(torch.int64)
+        assert bool((tm >= offd[te]).all()) and bool((tm < offd[te + 1]).all()), \
+            "token_index_map outside its expert's segment"
+        tok = torch.arange(t0, t1, device=dev, dtype=torch.int64).unsqueeze(1)
+        assert bool((eti[tm.reshape(-1)].to(torch.int64).view_as(tm) == tok).all()), \
+            "expert_token_indices[token_index_map] != token"
+        del te, tm, tok
+    assert np.array_equal(counts.cpu().numpy(), np.diff(offs)), "per-expert counts"
+    for e in range(E):
+        seg = eti[int(offs[e]):int(offs[e + 1])]
+        if seg.numel() > 1:
+            assert bool((seg[1:] > seg[:-1]).all()), f"expert {e}: tokens not ascending"
+    say(f"    {rows.size} sampled tokens bit-exact (gates max-abs {gerr:.1e}); "
+        f"properties hold on all {R} routes")
