@@ -51,6 +51,19 @@ def test_small_full(L, d, h, E, K, act, dt):
     run_full_parity(cfg, 11, require_gpu())
 
 
+# MOE_MAX_WIDTH of include/moe_dispatch.h, the largest d and h the FFN calls accept
+MAX_WIDTH = 1 << 20
+
+
+def test_max_width_full():
+    """The widest hidden layer the ABI accepts, h = MOE_MAX_WIDTH, in bf16,
+    whole tensors: every GEMM forms its in-tile offsets at their 32-bit bound
+    (256 rows of h bf16 values), the combine reduces over h and dx over 2h."""
+    cfg = W.small_config(300, 16, MAX_WIDTH, 3, 2, SWIGLU, W.BF16)
+    say(f"  {cfg.name}")
+    run_full_parity(cfg, 13, require_gpu())
+
+
 def _custom(cfg, seed, edit):
     dev = require_gpu()
     inp = W.make_inputs(cfg, seed, dev)
