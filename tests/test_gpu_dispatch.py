@@ -129,6 +129,41 @@ def test_dispatch_repeatable():
         assert torch.equal(getattr(a, n), getattr(b, n)), n
 
 
+def check_index_properties(L, E, K, eti, off, tei, tim, step=1 << 25):
+    """Properties that fix the four index structures uniquely once the
+    expert lists are known, checked on the device in chunks of tokens:
+    token_expert_indices rows strictly ascending in [0, E); offsets from 0 to
+    L*K with per-expert counts equal to the expert lists' histogram; each
+    segment of expert_token_indices strictly ascending; and
+    expert_token_indices[token_index_map[t, k]] = t, with token_index_map[t, k]
+    inside the segment of token_expert_indices[t, k].  Returns the offsets."""
+    dev = eti.device
+    R = L * K
+    offs = off.cpu().numpy().astype(np.int64)
+    assert offs[0] == 0 and offs[E] == R and np.all(np.diff(offs) >= 0), "offsets"
+    counts = torch.zeros(E, dtype=torch.int64, device=dev)
+    offd = off.to(torch.int64)
+    for t0 in range(0, L, step):
+        t1 = min(L, t0 + step)
+        te = tei[t0:t1].to(torch.int64)
+        assert bool((te >= 0).all()) and bool((te < E).all()), "expert id out of range"
+        assert bool((te[:, 1:] > te[:, :-1]).all()), "a token's experts not ascending"
+        counts += torch.bincount(te.reshape(-1), minlength=E)
+        tm = tim[t0:t1].to(torch.int64)
+        assert bool((tm >= offd[te]).all()) and bool((tm < offd[te + 1]).all()), \
+            "token_index_map outside its expert's segment"
+        tok = torch.arange(t0, t1, device=dev, dtype=torch.int64).unsqueeze(1)
+        assert bool((eti[tm.reshape(-1)].to(torch.int64).view_as(tm) == tok).all()), \
+            "expert_token_indices[token_index_map] != token"
+        del te, tm, tok
+    assert np.array_equal(counts.cpu().numpy(), np.diff(offs)), "per-expert counts"
+    for e in range(E):
+        seg = eti[int(offs[e]):int(offs[e + 1])]
+        if seg.numel() > 1:
+            assert bool((seg[1:] > seg[:-1]).all()), f"expert {e}: tokens not ascending"
+    return offs
+
+
 def test_dispatch_max_size():
     """The largest routing the ABI accepts at K = 8: L = 2^28 - 1 tokens
     (L * K = 2^31 - 8 routes, the last 64-token part ragged), E = 16.  The
@@ -159,8 +194,7 @@ def test_dispatch_max_size():
     B.moe_dispatch_build(shape, z, eti, off, tei, tim, gates)
     torch.cuda.synchronize()
 
-    offs = off.cpu().numpy().astype(np.int64)
-    assert offs[0] == 0 and offs[E] == R and np.all(np.diff(offs) >= 0)
+    check_index_properties(L, E, K, eti, off, tei, tim)
     # sampled tokens against the oracle (first, last and 4,096 random ones)
     gen = np.random.default_rng(7)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L),
@@ -170,27 +204,49 @@ def test_dispatch_max_size():
     assert np.array_equal(tei[ridx].cpu().numpy(), ref_tei), "sampled token_expert_indices"
     gerr = float(np.abs(gates[ridx].cpu().numpy().astype(np.float64) - ref_gates).max())
     assert gerr <= 1e-6, gerr
-    # whole-tensor properties, in chunks of tokens
-    counts = torch.zeros(E, dtype=torch.int64, device=dev)
-    offd = off.to(torch.int64)
-    step = 1 << 25
-    for t0 in range(0, L, step):
-        t1 = min(L, t0 + step)
-        te = tei[t0:t1].to(torch.int64)
-        assert bool((te >= 0).all()) and bool((te < E).all())
-        assert bool((te[:, 1:] > te[:, :-1]).all()), "a token's experts not ascending"
-        counts += torch.bincount(te.reshape(-1), minlength=E)
-        tm = tim[t0:t1].to(torch.int64)
-        assert bool((tm >= offd[te]).all()) and bool((tm < offd[te + 1]).all()), \
-            "token_index_map outside its expert's segment"
-        tok = torch.arange(t0, t1, device=dev, dtype=torch.int64).unsqueeze(1)
-        assert bool((eti[tm.reshape(-1)].to(torch.int64).view_as(tm) == tok).all()), \
-            "expert_token_indices[token_index_map] != token"
-        del te, tm, tok
-    assert np.array_equal(counts.cpu().numpy(), np.diff(offs)), "per-expert counts"
-    for e in range(E):
-        seg = eti[int(offs[e]):int(offs[e + 1])]
-        if seg.numel() > 1:
-            assert bool((seg[1:] > seg[:-1]).all()), f"expert {e}: tokens not ascending"
     say(f"    {rows.size} sampled tokens bit-exact (gates max-abs {gerr:.1e}); "
         f"properties hold on all {R} routes")
+
+
+@pytest.mark.parametrize("L,E,K", [
+    (3000, 16, 4),      # bit-mask router, direct-to-LDS rows
+    (5000, 64, 6),      # 64-expert router, rows through registers
+    (2000, 128, 8),     # wide router, two mask words
+    (1500, 1024, 8),    # wide router, sixteen mask words
+    (700, 32, 12),      # K > 8: byte map, one thread per token
+    (800, 200, 12),     # K > 8, E > 64: byte map, lane groups per token
+    (600, 30, 10),      # K > 8, E not a multiple of 4: lane groups, scalar loads
+])
+def test_dispatch_nonfinite_logits(L, E, K):
+    """Logits with NaN and infinite entries are outside the contract: the
+    results are unspecified but memory-safe, and every token still gets K
+    distinct experts, so the index structures keep all their properties.
+    Rows of finite logits route exactly as the oracle does."""
+    import oracle
+    from token_dispatch_expert_amd import binding as B
+
+    dev = require_gpu()
+    say(f"  dispatch L={L} E={E} K={K} with NaN / inf logits")
+    g = torch.Generator().manual_seed(L + E + K)
+    z = torch.randn(L, E, generator=g)
+    u = torch.rand(L, E, generator=g)
+    bad = torch.rand(L, generator=g) < 0.5          # half the tokens get non-finite entries
+    z[bad.unsqueeze(1) & (u < 0.10)] = float("nan")
+    z[bad.unsqueeze(1) & (u >= 0.10) & (u < 0.13)] = float("inf")
+    z[bad.unsqueeze(1) & (u >= 0.13) & (u < 0.16)] = float("-inf")
+    z[0] = float("nan")                             # a token with no finite logit
+    i32 = dict(dtype=torch.int32, device=dev)
+    eti, off = torch.empty(L * K, **i32), torch.empty(E + 1, **i32)
+    tei, tim = torch.empty(L, K, **i32), torch.empty(L, K, **i32)
+    gates = torch.empty(L, K, dtype=torch.float32, device=dev)
+    B.moe_dispatch_build(B.make_shape(L, 8, 8, E, K), z.to(dev), eti, off, tei, tim, gates)
+    torch.cuda.synchronize()
+    check_index_properties(L, E, K, eti, off, tei, tim)
+    fin = torch.isfinite(z).all(dim=1).numpy()
+    rows = np.flatnonzero(fin)
+    ref_tei, ref_gates = oracle.route(z.numpy()[rows], K)
+    assert np.array_equal(tei.cpu().numpy()[rows], ref_tei), "finite rows routed differently"
+    gerr = float(np.abs(gates.cpu().numpy()[rows].astype(np.float64) - ref_gates).max())
+    assert gerr <= 1e-6, gerr
+    say(f"    {int((~fin).sum())} tokens with non-finite logits: structures valid; "
+        f"{rows.size} finite rows bit-exact")

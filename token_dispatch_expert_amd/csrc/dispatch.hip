@@ -29,14 +29,22 @@ namespace moe {
 // G lanes cooperate on one token; lane j of the group owns experts
 // 4j .. 4j+3.  The K winners are found by K rounds of a group arg-max (ties
 // to the lower expert id); the softmax and the ascending-expert slot order
-// come from group reductions and a group prefix count.
+// come from group reductions and a group prefix count.  NaN logits (outside
+// the contract) rank as -inf in the arg-max, so a token with fewer than K
+// other logits still gets K distinct experts, filled from the lowest ids.
 template <int G>
 __device__ __forceinline__ void route_token(const float (&v)[4], int lg, int E, int K, int64_t t,
                                             int tl, int T, int32_t* __restrict__ tei,
                                             float* __restrict__ gates, uint8_t* smap) {
   int ev[4];
+  // selection key: a NaN logit (outside the contract) ranks as -inf, so that
+  // every round still finds an expert and each token gets K distinct ones
+  float key[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ev[j] = lg * 4 + j;
+  for (int j = 0; j < 4; ++j) {
+    ev[j] = lg * 4 + j;
+    key[j] = v[j] == v[j] ? v[j] : -INFINITY;
+  }
   unsigned sel = 0;
   float vmax = 0.f;
   for (int k = 0; k < K; ++k) {
@@ -45,8 +53,8 @@ __device__ __forceinline__ void route_token(const float (&v)[4], int lg, int E, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool cand = !((sel >> j) & 1u) && ev[j] < E;
-      if (cand && (v[j] > bv || (v[j] == bv && ev[j] < be))) {
-        bv = v[j];
+      if (cand && (key[j] > bv || (key[j] == bv && ev[j] < be))) {
+        bv = key[j];
         be = ev[j];
       }
     }
