@@ -42,7 +42,9 @@
  *     and float32 index/gate arrays must be 4-byte aligned.  Shapes outside
  *     these limits return MOE_ERR_UNSUPPORTED.
  *   - Router logits must be finite; NaN or infinite logits give unspecified
- *     (but memory-safe) results.
+ *     (but memory-safe) results: the gates are unspecified, yet every token
+ *     still receives K distinct experts, so the four index structures keep
+ *     their layout and stay valid inputs of the FFN calls.
  *   - Results are deterministic: repeated calls on the same inputs produce
  *     bitwise-identical outputs.
  */
