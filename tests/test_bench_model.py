@@ -67,3 +67,16 @@ def test_dispatch_bytes_bit_mask():
     # byte-map configurations (K > 8) count the map as 2LE (written, read)
     big = W.small_config(4096, 64, 64, 128, 12, W.SWIGLU, W.BF16)
     assert bench.dispatch_bytes(big) == 4 * 4096 * 128 + 16 * 4096 * 12 + 4 * 129 + 2 * 4096 * 128
+
+
+def test_more_than_one_gpu_refused():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says
+    so, before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr, r.stderr
