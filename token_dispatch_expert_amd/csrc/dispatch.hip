@@ -276,11 +276,12 @@ __device__ __forceinline__ int lowest_bit(uint64_t m) { return __builtin_ctzll(m
 // produce an invalid id: the mask is trimmed or filled to exactly K bits.
 //
 // Outputs besides tei and gates (the token-expert map of the method, in bit
-// form): each token's expert mask; for each part and expert e the wave
-// ballot col[part][e] (bit j set = token j of the part chose e); and the
-// part's per-expert counts cnt[e][part].
-// Transposes a wavefront's expert masks: for e in [E0, EB), lane e of
-// (hi:lo) receives the ballot of bit e of m (bit j = lane j has bit e set).
+// form): each token's expert mask; for each part and expert e the column
+// col[part][e] (bit j set = token j of the part chose e); and the part's
+// per-expert counts cnt[e][part].
+// Transposes a wavefront's expert masks one expert at a time (for masks of
+// at most 32 experts): for e in [E0, EB), lane e of (hi:lo) receives the
+// ballot of bit e of m (bit j = lane j has bit e set).
 template <int E0, int EB>
 struct BallotColumns {
   static __device__ __forceinline__ void run(uint64_t m, uint32_t& lo, uint32_t& hi) {
@@ -297,6 +298,29 @@ template <int EB>
 struct BallotColumns<EB, EB> {
   static __device__ __forceinline__ void run(uint64_t, uint32_t&, uint32_t&) {}
 };
+
+// 64 x 64 bit transpose across the wavefront: lane j holds row j (bit e =
+// token j chose expert e); on return lane e holds column e (bit j = token j
+// chose e).  Six exchange stages of the block transpose: at stage j the lane
+// pairs (k, k + j), k with lane bit j clear, swap the upper-right and
+// lower-left j x j blocks of their two rows.
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t x, int lane) {
+  constexpr uint64_t kMask[6] = {0x00000000FFFFFFFFull, 0x0000FFFF0000FFFFull,
+                                 0x00FF00FF00FF00FFull, 0x0F0F0F0F0F0F0F0Full,
+                                 0x3333333333333333ull, 0x5555555555555555ull};
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const int j = 32 >> s;
+    const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)x, j, 64);
+    const uint32_t phi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), j, 64);
+    const uint64_t y = ((uint64_t)phi << 32) | plo;
+    const bool top = (lane & j) == 0;
+    const uint64_t a = top ? x : y, b = top ? y : x;  // rows k and k + j
+    const uint64_t t = ((a >> j) ^ b) & kMask[s];
+    x ^= top ? (t << j) : t;
+  }
+  return x;
+}
 
 struct RouteSrc {
   const char* abase;  // logits rounded down to 16 bytes
@@ -428,11 +452,17 @@ __global__ __launch_bounds__(64) void k1_route_mask(const float* __restrict__ lo
   const float* row = reinterpret_cast<const float*>(stage + delta + lane * rowb);
   const uint64_t m = route_row<EB, KM, VEC>(row, E, K, lane, t < L, t, tei, gates);
   if (t < L) tmask[t] = m;
-  // one ballot per expert: the part's column of the map, kept by lane e
-  // (bits of experts >= E are clear, so their ballots are empty)
-  uint32_t col_lo = 0, col_hi = 0;
-  BallotColumns<0, EB>::run(m, col_lo, col_hi);
-  const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+  // the part's column of the map for expert e, kept by lane e (bits of
+  // experts >= E are clear, so their columns are empty): a bit transpose of
+  // the 64 masks for 64-expert rows, one ballot per expert for narrower ones
+  uint64_t mycol;
+  if constexpr (EB == 64) {
+    mycol = wave_transpose64(m, lane);
+  } else {
+    uint32_t col_lo = 0, col_hi = 0;
+    BallotColumns<0, EB>::run(m, col_lo, col_hi);
+    mycol = ((uint64_t)col_hi << 32) | col_lo;
+  }
   if (lane < E) {
     tcol[part * E + lane] = mycol;
     partcnt[(int64_t)lane * NP + part] = __popcll(mycol);
@@ -479,9 +509,7 @@ __global__ __launch_bounds__(64) void k1_route_mask64(const float* __restrict__ 
   const float* row = reinterpret_cast<const float*>(stage) + srow * E;
   const uint64_t m = route_row<64, KM, true>(row, E, K, lane, t < L, t, tei, gates);
   if (t < L) tmask[t] = m;
-  uint32_t col_lo = 0, col_hi = 0;
-  BallotColumns<0, 64>::run(m, col_lo, col_hi);
-  const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+  const uint64_t mycol = wave_transpose64(m, lane);  // m = 0 past L
   tcol[part * E + lane] = mycol;
   partcnt[(int64_t)lane * NP + part] = __popcll(mycol);
 }
@@ -637,8 +665,8 @@ __global__ __launch_bounds__(256) void k3_scatter_mask(const uint64_t* __restric
 // lane first); a shortfall (NaN logits, outside the contract) is filled with
 // the lowest unmarked ids, so every token gets exactly K valid experts.
 // Slots follow the lanes' order, hence ascending expert id.  The part's
-// masks collect in LDS as [token][word]; after the last round one ballot per
-// expert and word gives the part's columns.
+// masks collect in LDS as [token][word]; after the last round a bit transpose
+// of each word across the wavefront gives the part's columns.
 template <int P, int KM, bool VEC>
 __global__ __launch_bounds__(64) void k1_route_wide_mask(
     const float* __restrict__ logits, int64_t L, int E, int K, int64_t NP,
@@ -829,12 +857,9 @@ __global__ __launch_bounds__(64) void k1_route_wide_mask(
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  // columns: word qw of the part's 64 tokens -> one ballot per expert 64 qw + lane
+  // columns: word qw of the part's 64 tokens, transposed -> expert 64 qw + lane
   for (int qw = 0; qw < P; ++qw) {
-    const uint64_t mw = smask[lane][qw];
-    uint32_t col_lo = 0, col_hi = 0;
-    BallotColumns<0, 64>::run(mw, col_lo, col_hi);
-    const uint64_t mycol = ((uint64_t)col_hi << 32) | col_lo;
+    const uint64_t mycol = wave_transpose64(smask[lane][qw], lane);
     const int e = 64 * qw + lane;
     if (e < E) {
       tcol[part * E + e] = mycol;
