@@ -39,6 +39,7 @@ SMALL = [
     (800, 64, 128, 512, 6, SWIGLU, W.BF16),   # E = 512: about 9 routes per expert
     (600, 64, 64, 1024, 8, SILU, W.F32),      # E = 1024: many empty experts, fp32
     (300, 72, 136, 1000, 4, SWIGLU, W.BF16),  # E = 1000, ragged widths
+    (20000, 1024, 768, 16, 4, SWIGLU, W.F32),  # float32 at ~20 row tiles per expert, 4 slot passes
 ]
 
 
